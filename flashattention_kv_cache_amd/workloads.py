@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for exact-attention prefill and KV-cache decode.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the HIP path and the CPU oracle are fed from here,
+so they always see identical bits.
+
+Recipe (the same for every workload):
+  * one ``torch.Generator`` on the CPU seeded with ``seed``;
+  * Q/K/V and cache entries are i.i.d. N(0, 1) drawn in fp32, then rounded to
+    bf16 with round-to-nearest-even when the workload is bf16;
+  * cached lengths are integers drawn uniformly from [lo, hi], both ends
+    inclusive;
+  * a paged pool holds exactly sum_b ceil(L_b / block_size) blocks; physical
+    block ids are a seeded random permutation of the pool, handed out in
+    (sequence, logical block) order; unused block-table entries are -1;
+  * cache slots that no sequence owns (the tail of a contiguous row, the
+    unused slots of a sequence's last block) hold NaN, so a kernel that reads
+    them poisons its output.
+
+Layouts follow the pages' axis order: q/k/v ``(B, H, N, d)``; contiguous cache
+``(B, H_kv, S_cap, d)``; paged pool ``(num_blocks, block_size, H_kv, d)``
+("Module 09: Efficient Attention", section "Code: A Paged KV Cache from Scratch").
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _normal(gen: torch.Generator, shape, dtype: str, chunk: int = 1 << 26) -> torch.Tensor:
+    """N(0,1) fp32 draws rounded to ``dtype``; drawn in flat chunks so that a
+    multi-GiB bf16 pool never needs its fp32 copy in memory at once.  The
+    values do not depend on the chunk size (the generator is consumed in the
+    same order either way)."""
+    n = math.prod(shape)
+    out = torch.empty(n, dtype=_DTYPES[dtype])
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = torch.randn(e - s, generator=gen, dtype=torch.float32).to(out.dtype)
+    return out.view(*shape)
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    dtype: str
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def unmasked_pairs(self) -> int:
+        """Number of (query, key) pairs that enter the softmax, per (b, h)."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        off = self.Nk - self.Nq
+        return sum(min(self.Nk, i + off + 1) for i in range(self.Nq))
+
+    def flops(self) -> int:
+        """2 flop per multiply-add, 2*d MACs per pair (QK^T and PV)."""
+        return 4 * self.d * self.B * self.Hq * self.unmasked_pairs()
+
+    def algorithmic_bytes(self) -> int:
+        """Each input read once, each output written once (O plus fp32 LSE)."""
+        es = 4 if self.dtype == "f32" else 2
+        q = self.B * self.Hq * self.Nq * self.d * es
+        kv = 2 * self.B * self.Hkv * self.Nk * self.d * es
+        return q + kv + q + self.B * self.Hq * self.Nq * 4
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    len_lo: int
+    len_hi: int
+    paged: bool
+    dtype: str
+    seed: int
+    block_size: int = 16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+def prefill_inputs(w: PrefillWorkload):
+    """(q, k, v) on the CPU for a prefill workload."""
+    return make_prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+
+
+def make_prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = _normal(g, (B, Hq, Nq, d), dtype)
+    k = _normal(g, (B, Hkv, Nk, d), dtype)
+    v = _normal(g, (B, Hkv, Nk, d), dtype)
+    return q, k, v
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor                 # (B, Hq, d)
+    k_cache: torch.Tensor           # contiguous (B, Hkv, S_cap, d) or pool (nb, bs, Hkv, d)
+    v_cache: torch.Tensor
+    seq_lens: torch.Tensor          # (B,) int32
+    block_table: Optional[torch.Tensor]  # (B, max_blocks) int32 or None
+    block_size: int
+    kv_capacity: int                # S_cap, or number of pool blocks
+    max_seq_len: int                # host-side upper bound on seq_lens
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V that a decode step must read: 2*Hkv*d*elem per token."""
+        es = self.k_cache.element_size()
+        Hkv, d = self.k_cache.shape[2 if self.paged else 1], self.q.shape[-1]
+        return int(self.seq_lens.to(torch.int64).sum()) * 2 * Hkv * d * es
+
+
+def decode_inputs(w: DecodeWorkload) -> DecodeInputs:
+    return make_decode_inputs(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.seed,
+                              len_range=(w.len_lo, w.len_hi), paged=w.paged,
+                              block_size=w.block_size)
+
+
+def make_decode_inputs(B, Hq, Hkv, d, dtype, seed, len_range=None, seq_lens=None,
+                       paged=False, block_size=16, s_cap: Optional[int] = None,
+                       max_blocks: Optional[int] = None, spare_blocks: int = 0) -> DecodeInputs:
+    """Give either ``len_range=(lo, hi)`` (lengths drawn uniformly, inclusive)
+    or ``seq_lens`` (B explicit lengths).  ``spare_blocks`` adds pool blocks
+    that no sequence owns (all NaN)."""
+    g = torch.Generator().manual_seed(seed)
+    if seq_lens is None:
+        lo, hi = len_range
+        seq_lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64)
+        max_seq_len = hi
+    else:
+        seq_lens = torch.tensor(list(seq_lens), dtype=torch.int64)
+        assert seq_lens.numel() == B
+        max_seq_len = int(seq_lens.max()) if B > 0 else 0
+    q = _normal(g, (B, Hq, d), dtype)
+    if not paged:
+        cap = s_cap if s_cap is not None else max_seq_len
+        k = _normal(g, (B, Hkv, cap, d), dtype)
+        v = _normal(g, (B, Hkv, cap, d), dtype)
+        for b in range(B):
+            L = int(seq_lens[b])
+            k[b, :, L:, :] = float("nan")
+            v[b, :, L:, :] = float("nan")
+        return DecodeInputs(q, k, v, seq_lens.to(torch.int32), None, 0, cap, max_seq_len)
+    bs = block_size
+    nblk = [(int(L) + bs - 1) // bs for L in seq_lens]
+    total = sum(nblk) + spare_blocks
+    perm = torch.randperm(total, generator=g)
+    mb = max_blocks if max_blocks is not None else max(1, (max_seq_len + bs - 1) // bs)
+    table = torch.full((B, mb), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]].to(torch.int32)
+        off += nblk[b]
+    k = _normal(g, (total, bs, Hkv, d), dtype)
+    v = _normal(g, (total, bs, Hkv, d), dtype)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L % bs:
+            last = int(table[b, nblk[b] - 1])
+            k[last, L % bs:] = float("nan")
+            v[last, L % bs:] = float("nan")
+    for p in perm[sum(nblk):].tolist():      # spare blocks nobody owns
+        k[p] = float("nan")
+        v[p] = float("nan")
+    return DecodeInputs(q, k, v, seq_lens.to(torch.int32), table, bs, total, max_seq_len)
+
+
+# The five workloads: seeds are 1000 + index.  Head layouts follow the pages'
+# examples: 32 query / 8 KV heads of width 128 (Llama 3 8B style) and 64 / 8
+# (Llama 3 70B style); paged blocks of 16 tokens.
+C1 = PrefillWorkload("single-head non-causal fp32, N=256, d=64", 1, 1, 1, 256, 256, 64, False, "f32", 1000)
+C2 = PrefillWorkload("causal GQA prefill bf16, Hq=32 Hkv=8 N=4096 d=128", 1, 32, 8, 4096, 4096, 128, True, "bf16", 1001)
+C3 = DecodeWorkload("contiguous decode bf16, B=64 Hq=32 Hkv=8 d=128 L~U[1024,8192]", 64, 32, 8, 128, 1024, 8192, False, "bf16", 1002)
+C4 = PrefillWorkload("long-context causal GQA prefill bf16, Hq=64 Hkv=8 N=32768 d=128", 1, 64, 8, 32768, 32768, 128, True, "bf16", 1003)
+C5 = DecodeWorkload("paged decode bf16, B=128 Hq=32 Hkv=8 d=128 bs=16 L~U[512,32768]", 128, 32, 8, 128, 512, 32768, True, "bf16", 1004)
+WORKLOADS = (C1, C2, C3, C4, C5)
