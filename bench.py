@@ -1,0 +1,208 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+  * causal GQA prefill, bf16 in / fp32 accumulate: B=1, Hq=32, Hkv=8,
+    N=4096, d=128 (the workload the metric is quoted on), then
+  * paged KV-cache decode, bf16: B=128, Hq=32, Hkv=8, d=128, block 16, cached
+    lengths uniform in [512, 32768] (the metric's decode half).
+Inputs are generated once with the seeded recipe of
+flashattention_kv_cache_amd.workloads and copied to HBM before timing.
+
+Printed: one JSON line.  ``value`` is prefill TFLOP/s (algorithmic flops:
+2 per multiply-add, QK^T and PV over unmasked pairs only); the ``decode``
+object holds the decode KV GB/s (algorithmic bytes: every cached K/V byte once,
+plus q, o, lse and the block-table entries read).  Kernel durations come from
+HIP events recorded around each launch on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "prefill TFLOP/s & decode KV GB/s (% of MI355X peak), GQA d=128 bf16"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--split-tokens", type=int, default=0, help="decode tokens per split (0 = library choice)")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="after timing, run one device copy of this many MiB (a known-size kernel for HBM counters)")
+    return p.parse_args()
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workloads:
+    whole (b, h) heads of the prefill until about budget_s seconds have passed,
+    then a few decode sequences."""
+    import numpy as np
+    import oracle
+    from flashattention_kv_cache_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = W.C2
+    q, k, v = W.prefill_inputs(w)
+    n_rep = w.Hq // w.Hkv
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.Hq and time.perf_counter() - t0 < budget_s:
+        h = heads
+        g = h // n_rep
+        oracle.prefill(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], w.scale, True)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops_per_head = 4 * w.d * w.unmasked_pairs()
+    pre = flops_per_head * heads / dt / 1e12
+    # decode: a handful of whole sequences of the paged workload (all heads)
+    wd = W.C5
+    di = W.make_decode_inputs(8, wd.Hq, wd.Hkv, wd.d, "bf16", seed=wd.seed, len_range=(wd.len_lo, wd.len_hi),
+                              paged=True, block_size=wd.block_size)
+    t1 = time.perf_counter()
+    oracle.decode_paged(di.q, di.k_cache, di.v_cache, di.block_table, di.seq_lens, di.block_size, wd.scale)
+    ddt = time.perf_counter() - t1
+    dec = di.kv_bytes() / ddt / 1e9
+    return {"value": round(pre, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, causal prefill of {heads} of {w.Hq} query heads of the "
+                      f"N=4096 workload ({dt:.1f} s); decode of 8 paged sequences of the B=128 workload, "
+                      f"{int(di.seq_lens.sum())} tokens x 32 heads ({ddt:.1f} s)",
+            "decode_value": round(dec, 4), "decode_unit": "GB/s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from flashattention_kv_cache_amd import _build, binding
+    from flashattention_kv_cache_amd import workloads as W
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM before timing
+    wp = W.C2
+    q, k, v = W.prefill_inputs(wp)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wp.B, wp.Hq, wp.Nq), dtype=torch.float32, device=dev)
+    flops = wp.flops()
+
+    wd = W.C5
+    di = W.decode_inputs(wd)
+    dq, dk, dv = di.q.to(dev), di.k_cache.to(dev), di.v_cache.to(dev)
+    dl, dt_ = di.seq_lens.to(dev), di.block_table.to(dev)
+    do = torch.empty_like(dq)
+    dlse = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
+    split = args.split_tokens or binding.decode_split_tokens(wd.B, wd.Hq, wd.Hkv, wd.d, di.max_seq_len)
+    ws_bytes = binding.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.d, di.max_seq_len, split)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    nblk_read = int(((di.seq_lens.to(torch.int64) + wd.block_size - 1) // wd.block_size).sum())
+    kv_bytes = di.kv_bytes()
+    dec_bytes = kv_bytes + dq.numel() * 2 + do.numel() * 2 + dlse.numel() * 4 + nblk_read * 4 + wd.B * 4
+    del di
+
+    def prefill():
+        binding.prefill(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
+
+    def decode():
+        binding.decode(dq, dk, dv, dl, block_table=dt_, max_seq_len=wd.len_hi, scale=wd.scale,
+                       split_tokens=split, workspace=ws, out=do, lse=dlse)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        ev[i][2].record()
+        decode()
+        ev[i][3].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dec_ms = sorted(e[2].elapsed_time(e[3]) for e in ev)
+    pre_avg = sum(pre_ms) / K
+    dec_avg = sum(dec_ms) / K
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal GQA prefill bf16 B=1 Hq=32 Hkv=8 N=4096 d=128 + paged decode bf16 B=128 "
+                        "Hq=32 Hkv=8 d=128 block 16 L~U[512,32768]",
+            "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "N": wp.Nq, "d": wp.d, "causal": True,
+                        "seed": wp.seed, "flops": flops},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "block_size": wd.block_size,
+                       "len_range": [wd.len_lo, wd.len_hi], "seed": wd.seed, "tokens": kv_bytes // 4096,
+                       "split_tokens": split, "bytes": dec_bytes},
+        },
+        "prefill": {"value": round(tflops, 3), "unit": "TFLOP/s", "kernel_ms": round(pre_avg, 5),
+                    "kernel_ms_median": round(pre_ms[K // 2], 5), "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "decode": {"value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(dec_avg, 5),
+                   "kernel_ms_median": round(dec_ms[K // 2], 5), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_bf16_kernel<128>"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

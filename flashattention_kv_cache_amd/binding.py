@@ -1,0 +1,176 @@
+"""Python binding of libfa.so (include/fa.h): argument marshalling only.
+
+Tensors come from PyTorch (device memory and the current HIP stream); every
+step of the computation runs in the library's HIP kernels.  If the library is
+not built, or no GPU is present, calls raise — there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from ._build import LIB_PATH
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_BF16 = 0, 1
+
+# Every symbol include/fa.h declares, with its ctypes signature.
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_abi_version": ([], _I),
+    "fa_status_string": ([_I], ctypes.c_char_p),
+    "fa_last_error": ([], ctypes.c_char_p),
+    "fa_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
+    "fa_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _S),
+    "fa_decode_split_tokens": ([_I, _I, _I, _I, _I], _I),
+    "fa_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P], _I),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run flashattention_kv_cache_amd._build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().fa_status_string(s).decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FAError(status, lib().fa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fa_prefill: q (B, Hq, Nq, d), k/v (B, Hkv, Nk, d) -> (o, lse)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q (B,Hq,Nq,d) and k, v (B,Hkv,Nk,d)")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, dk = k.shape
+    if k.shape[0] != B or dk != d or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v disagree in batch, head dim or dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().fa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                            B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                            _dtype_code(q), _stream(stream)))
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens))
+
+
+def decode_split_tokens(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int) -> int:
+    return int(lib().fa_decode_split_tokens(B, Hq, Hkv, d, max_seq_len))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+           block_table: Optional[torch.Tensor] = None, block_size: int = 0,
+           max_seq_len: Optional[int] = None, scale: Optional[float] = None,
+           split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fa_decode: q (B, Hq, d) against a contiguous cache (B, Hkv, S_cap, d) or,
+    with ``block_table`` (B, max_blocks) int32, a paged pool
+    (num_blocks, block_size, Hkv, d).  ``max_seq_len`` bounds seq_lens; it
+    defaults to the capacity of the layout (no device read-back)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    B, Hq, d = q.shape
+    paged = block_table is not None
+    if paged:
+        _dev(block_table, "block_table")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 (B, max_blocks)")
+        nblk, bs, Hkv, dk = k_cache.shape
+        if block_size and block_size != bs:
+            raise ValueError("block_size disagrees with the pool shape")
+        block_size = bs
+        capacity = nblk
+        max_blocks = block_table.shape[1]
+        bound = max_blocks * bs
+    else:
+        Bc, Hkv, cap, dk = k_cache.shape
+        if Bc != B:
+            raise ValueError("cache batch != q batch")
+        capacity = cap
+        max_blocks = 0
+        bound = cap
+    if dk != d or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches disagree in head dim, shape or dtype")
+    if max_seq_len is None:
+        max_seq_len = bound
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+                           block_size if paged else 0, max_blocks, capacity, int(max_seq_len),
+                           _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
+                           int(split_tokens), _ptr(workspace) if need else None, ws_bytes,
+                           _stream(stream)))
+    return out, lse

@@ -1,0 +1,329 @@
+// Single-token decode against a contiguous or paged KV cache: split-K partial
+// kernel plus a log-sum-exp merge kernel.
+//
+// What is computed: one new query per (sequence, query head) against every
+// cached key of the sequence, the new token included, no mask ("Генерация и
+// KV-кэш", section "KV-кэш для одной головы на NumPy"); query head h reads KV
+// head floor(h / n_rep) ("Module 09: Efficient Attention", "The Math: Sharing
+// Keys and Values"); paged token t sits at (block_table[t / bs], t % bs) of a
+// (num_blocks, bs, Hkv, d) pool ("Module 09", "Code: A Paged KV Cache from
+// Scratch").
+//
+// Decode reads every cached byte once and does 4 flop per byte of bf16 cache,
+// so it is bound by HBM bandwidth.  The design is about streaming:
+//   * a workgroup owns (sequence b, KV head g, a group of QH query heads of g,
+//     split s) and reads split s of g's keys and values exactly once for all
+//     QH heads;
+//   * a token row (d elements) is read by G = d/16 lanes, 16 elements each, as
+//     16-byte loads; a wave covers 64/G tokens per load and issues U such loads
+//     for K and for V before using any of them;
+//   * scores are reduced across the G lanes with DPP, and each G-lane group
+//     keeps its own running (max, sum, output) — the recurrence of the "Li
+//     Hongyi, Machine Learning 2026" notes, lecture "FlashAttention" — so the
+//     loop has no cross-group traffic; the groups, then the four waves, are
+//     combined once at the end;
+//   * the partial (normalised output, log-sum-exp) of each split goes to the
+//     workspace and a second kernel merges a sequence's splits with weights
+//     exp(lse_s - max lse) — the same recurrence applied to whole splits.  A
+//     sequence that fits in one split is written directly.
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kU = 4;          // token loads per wave per iteration
+constexpr int kElems = 16;     // elements of a row held by one lane
+
+template <typename T> struct Elem;
+template <> struct Elem<float> { static constexpr int kVecs = 4; };     // 16 floats = 4 x 16 B
+template <> struct Elem<uint16_t> { static constexpr int kVecs = 2; };  // 16 bf16  = 2 x 16 B
+
+// Partial dot product of a lane's 16 elements of q and k.
+__device__ __forceinline__ float dot16(const u32x4_t* q, const u32x4_t* k, float) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = fmaf(__uint_as_float(q[j][t]), __uint_as_float(k[j][t]), acc);
+  return acc;
+}
+__device__ __forceinline__ float dot16(const u32x4_t* q, const u32x4_t* k, uint16_t) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[j][t]), as_bf16x2(k[j][t]), acc, false);
+  return acc;
+}
+
+// o[0..15] += p * v (the lane's 16 elements, in the lane's element order).
+__device__ __forceinline__ void axpy16(float* o, float p, const u32x4_t* v, float) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[j * 4 + t] = fmaf(p, __uint_as_float(v[j][t]), o[j * 4 + t]);
+}
+__device__ __forceinline__ void axpy16(float* o, float p, const u32x4_t* v, uint16_t) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o[j * 8 + 2 * t] = fmaf(p, bf16lo_to_f32(v[j][t]), o[j * 8 + 2 * t]);
+      o[j * 8 + 2 * t + 1] = fmaf(p, bf16hi_to_f32(v[j][t]), o[j * 8 + 2 * t + 1]);
+    }
+}
+
+// Index in the d-vector of element i (0..15) held by lane `sub` of a G-lane group.
+template <typename T, int G>
+__device__ __forceinline__ int elem_index(int sub, int i) {
+  constexpr int per = 16 / (int)sizeof(T);         // elements per 16-byte vector
+  return ((i / per) * G + sub) * per + (i % per);
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  if constexpr (G == 8) x += dpp<kDppHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ int num_splits(int L, int max_seq_len, int chunk) {
+  if (L < 0 || L > max_seq_len) return 1;  // invalid length: reported by split 0 as NaN
+  return L <= chunk ? 1 : (L + chunk - 1) / chunk;
+}
+
+// Combine running state (m, l, o) with (m2, l2, o2); m are log2-domain maxima.
+template <int N>
+__device__ __forceinline__ void combine(float& m, float& l, float* o, float m2, float l2, const float* o2) {
+  const float mn = fmaxf(m, m2);
+  const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+  const float a2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mn);
+  l = l * a1 + l2 * a2;
+#pragma unroll
+  for (int i = 0; i < N; ++i) o[i] = o[i] * a1 + o2[i] * a2;
+  m = mn;
+}
+
+template <typename T, int D, int QH, bool PAGED>
+__global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a) {
+  constexpr int G = D / kElems;         // lanes per token row
+  constexpr int TPW = 64 / G;           // tokens per wave per load
+  constexpr int NV = Elem<T>::kVecs;    // 16-byte vectors per lane per row
+  constexpr int TOK_IT = TPW * kU;      // tokens per wave per iteration
+
+  __shared__ float red_o[kWaves][QH][D];
+  __shared__ float red_ml[kWaves][QH][2];
+  __shared__ int red_bad[kWaves];
+
+  const int s = blockIdx.x;
+  const int nqg = (a.Hq / a.Hkv) / QH;
+  const int g = blockIdx.y / nqg;
+  const int h0 = g * (a.Hq / a.Hkv) + (blockIdx.y % nqg) * QH;
+  const int b = blockIdx.z;
+
+  const int L = a.seq_lens[b];
+  const int ns = num_splits(L, a.max_seq_len, a.split_tokens);
+  if (s >= ns) return;
+  bool bad = (L < 0 || L > a.max_seq_len);
+  const int t_begin = bad ? 0 : s * a.split_tokens;
+  const int t_end = bad ? 0 : min(L, t_begin + a.split_tokens);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane / G;
+  const int sub = lane % G;
+  const float c = a.scale * kLog2e;
+
+  // this lane's 16 elements of each query head
+  u32x4_t q[QH][NV];
+  {
+    const u32x4_t* qv = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + h0) * D);
+#pragma unroll
+    for (int r = 0; r < QH; ++r)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) q[r][j] = qv[r * (D * sizeof(T) / 16) + j * G + sub];
+  }
+
+  float m[QH], l[QH], o[QH][kElems];
+#pragma unroll
+  for (int r = 0; r < QH; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) o[r][i] = 0.f;
+  }
+
+  const size_t row_vecs = D * sizeof(T) / 16;  // 16-byte vectors per token row
+  const u32x4_t* kbase = reinterpret_cast<const u32x4_t*>(a.k);
+  const u32x4_t* vbase = reinterpret_cast<const u32x4_t*>(a.v);
+  const int32_t* table = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
+  const size_t contig_base = ((size_t)b * a.Hkv + g) * (size_t)a.kv_capacity;
+
+  for (int t0 = t_begin + wave * TOK_IT; t0 < t_end; t0 += kWaves * TOK_IT) {
+    u32x4_t kr[kU][NV], vr[kU][NV];
+    bool ok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tok = t0 + u * TPW + grp;
+      ok[u] = tok < t_end;
+      size_t row = 0;
+      if (ok[u]) {
+        if constexpr (PAGED) {
+          int phys = table[tok >> a.log2_block_size];
+          if (phys < 0 || phys >= a.kv_capacity) { bad = true; phys = 0; }
+          row = ((size_t)phys * a.block_size + (tok & (a.block_size - 1))) * a.Hkv + g;
+        } else {
+          row = contig_base + tok;
+        }
+      }
+      const size_t base = row * row_vecs + sub;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        kr[u][j] = ok[u] ? kbase[base + j * G] : u32x4_t{0, 0, 0, 0};
+        vr[u][j] = ok[u] ? vbase[base + j * G] : u32x4_t{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < QH; ++r) {
+      float sc[kU];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float part = dot16(q[r], kr[u], T{});
+        sc[u] = ok[u] ? group_sum<G>(part) * c : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      const float mn = fmaxf(m[r], mx);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m[r] - mu);
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        sc[u] = fast_exp2(sc[u] - mu);
+        psum += sc[u];
+      }
+      l[r] = l[r] * alpha + psum;
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) o[r][i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) axpy16(o[r], sc[u], vr[u], T{});
+      m[r] = mn;
+    }
+  }
+
+  // combine the TPW groups of this wave (lanes with equal `sub`)
+#pragma unroll
+  for (int x = G; x < 64; x <<= 1) {
+#pragma unroll
+    for (int r = 0; r < QH; ++r) {
+      float o2[kElems];
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) o2[i] = __shfl_xor(o[r][i], x);
+      const float m2 = __shfl_xor(m[r], x);
+      const float l2 = __shfl_xor(l[r], x);
+      combine<kElems>(m[r], l[r], o[r], m2, l2, o2);
+    }
+  }
+  const bool wave_bad = __any(bad);
+  if (lane < G) {
+#pragma unroll
+    for (int r = 0; r < QH; ++r) {
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) red_o[wave][r][elem_index<T, G>(sub, i)] = o[r][i];
+      if (sub == 0) {
+        red_ml[wave][r][0] = m[r];
+        red_ml[wave][r][1] = l[r];
+      }
+    }
+  }
+  if (lane == 0) red_bad[wave] = wave_bad;
+  __syncthreads();
+
+  const bool any_bad = red_bad[0] | red_bad[1] | red_bad[2] | red_bad[3];
+  for (int idx = threadIdx.x; idx < QH * D; idx += kWaves * 64) {
+    const int r = idx / D, e = idx % D;
+    float mm = red_ml[0][r][0], ll = red_ml[0][r][1], oo = red_o[0][r][e];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) combine<1>(mm, ll, &oo, red_ml[w][r][0], red_ml[w][r][1], &red_o[w][r][e]);
+    const int h = h0 + r;
+    float out = ll > 0.f ? oo / ll : 0.f;
+    float lse = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
+    if (any_bad) out = lse = NAN;
+    if (ns == 1) {
+      if constexpr (sizeof(T) == 4) {
+        reinterpret_cast<float*>(a.o)[((size_t)b * a.Hq + h) * D + e] = out;
+      } else {
+        const uint32_t pk = pack_bf16x2(out, 0.f);
+        reinterpret_cast<uint16_t*>(a.o)[((size_t)b * a.Hq + h) * D + e] = (uint16_t)(pk & 0xffffu);
+      }
+      if (a.lse && e == 0) a.lse[(size_t)b * a.Hq + h] = lse;
+    } else {
+      const size_t slot = ((size_t)b * a.Hq + h) * a.max_splits + s;
+      a.ws_o[slot * D + e] = out;
+      if (e == 0) a.ws_lse[slot] = lse;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int L = a.seq_lens[b];
+  const int ns = num_splits(L, a.max_seq_len, a.split_tokens);
+  if (ns == 1) return;  // written by the split kernel
+  const size_t slot0 = (size_t)bh * a.max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[slot0 + s]);
+  const int e = threadIdx.x;
+  float wsum = 0.f, acc = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = __expf(a.ws_lse[slot0 + s] - M);
+    wsum += w;
+    if (e < a.d) acc = fmaf(w, a.ws_o[(slot0 + s) * a.d + e], acc);
+  }
+  if (e < a.d) {
+    const float out = acc / wsum;
+    if constexpr (sizeof(T) == 4) {
+      reinterpret_cast<float*>(a.o)[(size_t)bh * a.d + e] = out;
+    } else {
+      reinterpret_cast<uint16_t*>(a.o)[(size_t)bh * a.d + e] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
+    }
+  }
+  if (a.lse && e == 0) a.lse[bh] = M + __logf(wsum);
+}
+
+template <typename T, int D, int QH>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
+  const int nqg = (a.Hq / a.Hkv) / QH;
+  dim3 grid(a.max_splits, a.Hkv * nqg, a.B);
+  if (a.block_table)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, QH, true>), grid, dim3(kWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, QH, false>), grid, dim3(kWaves * 64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_splits == 1) return e;
+  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3(a.B * a.Hq), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
+  const int n_rep = a.Hq / a.Hkv;
+  if (n_rep % 8 == 0) return launch_typed<T, D, 8>(a, st);
+  if (n_rep % 4 == 0) return launch_typed<T, D, 4>(a, st);
+  if (n_rep % 2 == 0) return launch_typed<T, D, 2>(a, st);
+  return launch_typed<T, D, 1>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t st) {
+  if (bf16) return a.d == 64 ? launch_d<uint16_t, 64>(a, st) : launch_d<uint16_t, 128>(a, st);
+  return a.d == 64 ? launch_d<float, 64>(a, st) : launch_d<float, 128>(a, st);
+}
+
+}  // namespace fa

@@ -1,0 +1,191 @@
+// Host side of the C ABI declared in include/fa.h: argument checks (all done
+// before any HIP call), launch planning, and error reporting.
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(fa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Tokens per decode split when the caller leaves the choice to the library:
+// aim for about 8192 splits over (sequence, KV head group) pairs if every
+// sequence had max_seq_len tokens, with at least 256 and at most 4096 tokens
+// per split (a power of two).
+int choose_split_tokens(int B, int Hq, int Hkv, int max_seq_len) {
+  const int n_rep = Hq / Hkv;
+  const int qh = n_rep % 8 == 0 ? 8 : n_rep % 4 == 0 ? 4 : n_rep % 2 == 0 ? 2 : 1;
+  const double pairs = (double)B * Hkv * (n_rep / qh);
+  double want = pairs * (double)max_seq_len / 8192.0;
+  int st = 256;
+  while (st < 4096 && st * 2 <= want) st *= 2;
+  return st;
+}
+
+int check_decode_sizes(int B, int Hq, int Hkv, int d, int max_seq_len, int split_tokens) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || max_seq_len < 0)
+    return fail(FA_ERR_INVALID, "B=%d Hq=%d Hkv=%d max_seq_len=%d: need B >= 0, heads >= 1, max_seq_len >= 0",
+                B, Hq, Hkv, max_seq_len);
+  if (Hq % Hkv) return fail(FA_ERR_INVALID, "num_kv_heads (%d) must divide num_heads (%d)", Hkv, Hq);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64 or 128)", d);
+  if (split_tokens < 0 || split_tokens % 256)
+    return fail(FA_ERR_INVALID, "split_tokens %d must be 0 or a positive multiple of 256", split_tokens);
+  return FA_OK;
+}
+
+int max_splits_for(int max_seq_len, int split_tokens) {
+  return max_seq_len <= split_tokens ? 1 : (max_seq_len + split_tokens - 1) / split_tokens;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 1; }
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               int causal, float scale, int dtype, void* stream) {
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1)
+    return fail(FA_ERR_INVALID, "B=%d Hq=%d Hkv=%d Nq=%d Nk=%d: sizes must be >= 0 and heads >= 1", B, Hq, Hkv, Nq, Nk);
+  if (Hq % Hkv) return fail(FA_ERR_INVALID, "num_kv_heads (%d) must divide num_heads (%d)", Hkv, Hq);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64 or 128)", d);
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (causal && Nq > Nk)
+    return fail(FA_ERR_INVALID, "causal attention with Nq=%d > Nk=%d would leave rows with no visible key", Nq, Nk);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
+  if (B == 0 || Nq == 0) return ok();
+  if (!q || !o || (Nk > 0 && (!k || !v))) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const long long rows = (long long)B * Hq * Nq;
+  if (rows * d >= (1ll << 40)) return fail(FA_ERR_UNSUPPORTED, "problem too large");
+
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dtype == FA_BF16 ? fa::launch_prefill_bf16(a, st) : fa::launch_prefill_f32(a, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len) {
+  if (check_decode_sizes(B, Hq, Hkv, d, max_seq_len, 0) != FA_OK) return 0;
+  return choose_split_tokens(B, Hq, Hkv, max_seq_len);
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len, int split_tokens) {
+  if (check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens) != FA_OK) return 0;
+  const int st = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, max_seq_len);
+  const int ns = max_splits_for(max_seq_len, st);
+  if (ns <= 1) return 0;
+  const size_t slots = (size_t)B * Hq * ns;
+  // partial outputs (d floats per slot) then partial LSEs, each 256-byte aligned
+  const size_t o_bytes = (slots * d * sizeof(float) + 255) & ~(size_t)255;
+  const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
+  return o_bytes + l_bytes;
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* seq_lens, const int32_t* block_table,
+              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+              void* o, float* lse,
+              int B, int Hq, int Hkv, int d, float scale, int dtype,
+              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  int st0 = check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens);
+  if (st0 != FA_OK) return st0;
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (!is_pow2(block_size) || block_size > 1024)
+      return fail(FA_ERR_INVALID, "block_size %d must be a power of two in [1, 1024]", block_size);
+    if (kv_capacity < 1) return fail(FA_ERR_INVALID, "paged pool must hold at least one block");
+    if ((long long)max_blocks_per_seq * block_size < max_seq_len)
+      return fail(FA_ERR_INVALID, "max_blocks_per_seq (%d) * block_size (%d) < max_seq_len (%d)",
+                  max_blocks_per_seq, block_size, max_seq_len);
+  } else {
+    if (kv_capacity < max_seq_len)
+      return fail(FA_ERR_INVALID, "contiguous cache capacity %d < max_seq_len %d", kv_capacity, max_seq_len);
+  }
+  if (B == 0) return ok();
+  if (!q || !k_cache || !v_cache || !seq_lens || !o) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return fail(FA_ERR_INVALID, "seq_lens and block_table must be 4-byte aligned");
+  if (kv_capacity < 1) return fail(FA_ERR_INVALID, "KV capacity must be >= 1");
+
+  const int stoks = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, max_seq_len);
+  const int ns = max_splits_for(max_seq_len, stoks);
+  const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_INVALID, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
+  if (B > 65535 || Hq > 65535) return fail(FA_ERR_UNSUPPORTED, "grid too large (B and Hq must be <= 65535)");
+
+  fa::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.block_table = block_table;
+  a.block_size = paged ? block_size : 0;
+  a.log2_block_size = paged ? ilog2(block_size) : 0;
+  a.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  a.kv_capacity = kv_capacity; a.max_seq_len = max_seq_len;
+  a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = scale;
+  a.split_tokens = stoks; a.max_splits = ns;
+  if (ns > 1) {
+    const size_t slots = (size_t)B * Hq * ns;
+    const size_t o_bytes = (slots * d * sizeof(float) + 255) & ~(size_t)255;
+    a.ws_o = reinterpret_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+  }
+  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Internal declarations shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// ---------------------------------------------------------------------------
+// Launch descriptors (host side fills, launchers consume).
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  int causal;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* block_table;  // nullptr: contiguous layout
+  int block_size, log2_block_size, max_blocks_per_seq;
+  int kv_capacity, max_seq_len;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, d;
+  float scale;
+  int split_tokens;   // tokens per split (multiple of 256)
+  int max_splits;     // ceil(max_seq_len / split_tokens), >= 1
+  float* ws_o;        // (B, Hq, max_splits, d) partial outputs, when max_splits > 1
+  float* ws_lse;      // (B, Hq, max_splits) partial log-sum-exp
+};
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values packed into one dword
+// (lo = a, hi = b); gfx950 has a single instruction for it.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r = {(__bf16)a, (__bf16)b};  // lowers to v_cvt_pk_bf16_f32
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// DPP lane exchanges inside a row of 16 lanes.
+enum : int {
+  kDppXor1 = 0xB1,         // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,         // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,  // lane i <-> 7-i within each 8 lanes
+  kDppMirror = 0x140,      // lane i <-> 15-i within each 16 lanes
+  kDppRor8 = 0x128,        // rotate right by 8 within each 16 lanes
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// v_permlane32_swap exchanges the upper half of one register with the lower
+// half of another.  Applied to two copies of x, lane l ends up holding the
+// pair {x[l % 32], x[l % 32 + 32]} across the two results, so the max and the
+// sum of the two are the combine of lane l with lane l ^ 32 (whichever result
+// holds which half).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reinterpret a dword as two bf16.  Goes through a scalar copy: this clang
+// miscompiles __builtin_bit_cast applied directly to an ext_vector element
+// subscript (it reads element 0 whatever the index).
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+  bf16x2_t r;
+  __builtin_memcpy(&r, &w, sizeof r);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace fa

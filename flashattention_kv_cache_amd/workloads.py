@@ -23,7 +23,9 @@ Layouts follow the pages' axis order: q/k/v ``(B, H, N, d)``; contiguous cache
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -32,16 +34,34 @@ import torch
 _DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def _normal(gen: torch.Generator, shape, dtype: str, chunk: int = 1 << 26) -> torch.Tensor:
-    """N(0,1) fp32 draws rounded to ``dtype``; drawn in flat chunks so that a
-    multi-GiB bf16 pool never needs its fp32 copy in memory at once.  The
-    values do not depend on the chunk size (the generator is consumed in the
-    same order either way)."""
+_CHUNK = 1 << 24  # elements per independently seeded chunk
+
+
+def _normal(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
+    """N(0,1) fp32 draws rounded to ``dtype``.
+
+    One 62-bit base seed is drawn from ``gen``; element chunk c (of a fixed
+    2^24 elements) is drawn from a fresh generator seeded base + c.  The values
+    therefore depend only on (gen's state, shape), not on how many threads fill
+    the chunks, and multi-GiB pools are generated in parallel without an fp32
+    copy of the whole tensor."""
     n = math.prod(shape)
+    base = int(torch.randint(0, 2 ** 62, (1,), generator=gen, dtype=torch.int64))
     out = torch.empty(n, dtype=_DTYPES[dtype])
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = torch.randn(e - s, generator=gen, dtype=torch.float32).to(out.dtype)
+
+    def fill(c: int):
+        s, e = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        g = torch.Generator().manual_seed(base + c)
+        out[s:e] = torch.randn(e - s, generator=g, dtype=torch.float32).to(out.dtype)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        workers = min(nchunks, max(1, min(16, os.cpu_count() or 1)))
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.view(*shape)
 
 

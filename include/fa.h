@@ -1,0 +1,161 @@
+/*
+ * fa.h — exact softmax attention on AMD Instinct MI355X (gfx950): tiled
+ * prefill with the online-softmax recurrence, and single-token decode against
+ * a contiguous or paged KV cache.
+ *
+ * C ABI.  Plain pointers and sizes; no C++ or framework types cross it.
+ *
+ * Ownership and execution model (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees, or synchronises: work is enqueued on
+ *     `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *     the call returns without waiting for it.
+ *   - Tensors are dense and row-major with the head dimension innermost, in the
+ *     axis order given with each call; every pointer must be 16-byte aligned.
+ *   - Arguments are checked on the host before any HIP call.  A rejected call
+ *     returns FA_ERR_INVALID or FA_ERR_UNSUPPORTED and enqueues nothing.  A
+ *     failed kernel launch returns FA_ERR_HIP.  No exception crosses the ABI.
+ *   - The library is stateless apart from a thread-local error message and is
+ *     safe to call from several host threads.
+ *   - Outputs are deterministic: the same inputs and launch configuration give
+ *     the same bits (no atomics).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID = 1,     /* an argument breaks the contract below            */
+  FA_ERR_UNSUPPORTED = 2, /* valid in principle, not built (e.g. head dim 96) */
+  FA_ERR_HIP = 3          /* the HIP runtime reported an error                */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_F32 = 0,  /* fp32 in, fp32 out, fp32 arithmetic                       */
+  FA_BF16 = 1  /* bf16 in, bf16 out (round to nearest even), fp32 accumulate */
+} fa_dtype;
+
+/* Version of this ABI (bumped on any signature change). */
+int fa_abi_version(void);
+
+/* Static description of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Detail for the last non-OK status returned on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+/*
+ * fa_prefill — attention of every query row against the keys, computed in
+ * tiles with the streaming softmax (running max and running sum, earlier
+ * partial results rescaled when the max grows), so the Nq x Nk score matrix is
+ * never written to memory.
+ *
+ * Defined by: "KV Cache, Flash Attention and Inference Optimization" (AI
+ * Engineering from Scratch, phase 07 lesson 12), section "the tiling trick"
+ * (outer loop over query tiles, inner loop over key/value tiles, one write of
+ * the output tile); "Module 09: Efficient Attention", sections "The Math:
+ * Sharing Keys and Values" (softmax(QK^T/sqrt(d_k))V with query head h reading
+ * key/value head floor(h / (Hq/Hkv))) and "FlashAttention: The Compute Wall"
+ * (the streaming identity); "Li Hongyi, Machine Learning 2026" notes, lecture
+ * "FlashAttention" (the running max/sum recurrence).
+ *
+ *   q   (B, Hq,  Nq, d)   input dtype
+ *   k   (B, Hkv, Nk, d)   input dtype
+ *   v   (B, Hkv, Nk, d)   input dtype
+ *   o   (B, Hq,  Nq, d)   output, input dtype
+ *   lse (B, Hq,  Nq)      fp32 output or NULL: natural log of the sum over
+ *                         visible keys of exp(scale * q.k); -inf for a row that
+ *                         sees no key
+ *   scale                 multiplies q.k before the softmax (finite, > 0;
+ *                         1/sqrt(d) for the usual attention)
+ *   causal                0: every key visible.  1: key j visible to query i
+ *                         iff j <= i + (Nk - Nq), the mask aligned to the
+ *                         bottom-right corner so that Nq new queries appended to
+ *                         Nk - Nq cached keys see the whole past ("Генерация и
+ *                         KV-кэш", section "Три ловушки", item 2)
+ *
+ * Contract: B, Nq, Nk >= 0; Hq, Hkv >= 1; Hq % Hkv == 0; d in {64, 128};
+ * causal requires Nq <= Nk (otherwise rows with no visible key would exist).
+ * Nk == 0 (non-causal) yields o = 0 and lse = -inf.  B == 0 or Nq == 0 is a
+ * no-op.  q, k, v must not alias o or lse.
+ */
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_decode_workspace_bytes — bytes of device workspace fa_decode needs for
+ * these sizes (0 when every sequence fits in one split).  `split_tokens` is
+ * the same value that will be passed to fa_decode (0 = library choice).
+ * Returns 0 for arguments fa_decode would reject.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len,
+                                 int split_tokens);
+
+/*
+ * fa_decode_split_tokens — tokens per split that fa_decode uses for these
+ * sizes when called with split_tokens = 0.
+ */
+int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len);
+
+/*
+ * fa_decode — one new query per (sequence, query head) against all of that
+ * sequence's cached keys and values, the new token's own included (it is
+ * already in the cache and counted by seq_lens); no mask.
+ *
+ * Defined by: "Генерация и KV-кэш" (ai.flicky.cc, stage 4.6 lesson 04),
+ * section "KV-кэш для одной головы на NumPy" (decode step = softmax of the new
+ * query against every cached key, weighted sum of cached values); "Module 09:
+ * Efficient Attention", sections "Code: Cache-Aware Grouped-Query Attention"
+ * (the cache stores only Hkv heads) and "Code: A Paged KV Cache from Scratch"
+ * (pool of fixed-size blocks, token t of a sequence at
+ * (block_table[t / block_size], t % block_size)).
+ *
+ * The keys of each sequence are cut into splits of `split_tokens`; each split
+ * produces a partial (output, log-sum-exp) and a second pass merges the
+ * partials of a sequence with weights exp(lse_s - max_s lse_s).
+ *
+ *   q            (B, Hq, d)              input dtype
+ *   k_cache,     contiguous: (B, Hkv, kv_capacity, d), row L_b.. unused
+ *   v_cache      paged:      (kv_capacity, block_size, Hkv, d) shared pool
+ *   seq_lens     (B) int32, device: cached length L_b of each sequence
+ *   block_table  NULL for the contiguous layout, else (B, max_blocks_per_seq)
+ *                int32, device: physical block of each logical block; only the
+ *                first ceil(L_b / block_size) entries of a row are read
+ *   block_size   paged: tokens per block, a power of two in [1, 1024]
+ *   max_blocks_per_seq  paged: row length of block_table
+ *   kv_capacity  contiguous: S_cap (>= max_seq_len); paged: pool blocks
+ *   max_seq_len  host-side upper bound on every L_b (sizes the launch without
+ *                reading seq_lens back)
+ *   o            (B, Hq, d) output, input dtype
+ *   lse          (B, Hq) fp32 output or NULL
+ *   split_tokens 0 = library choice, else tokens per split: a multiple of 256
+ *   workspace    device scratch of fa_decode_workspace_bytes(...) bytes, or
+ *                NULL when that is 0; contents on entry are ignored
+ *
+ * Contract: B >= 0; Hq % Hkv == 0; d in {64, 128}; 0 <= L_b <= max_seq_len;
+ * for the paged layout every read block id lies in [0, kv_capacity) and
+ * max_blocks_per_seq * block_size >= max_seq_len.  L_b == 0 yields o = 0 and
+ * lse = -inf.  Device-side violations (an L_b outside [0, max_seq_len], an
+ * out-of-range block id) are detected by the kernel: that sequence's rows of
+ * o and lse come out NaN and no out-of-range address is read.
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* seq_lens, const int32_t* block_table,
+              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+              void* o, float* lse,
+              int B, int Hq, int Hkv, int d, float scale, int dtype,
+              int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects every contract violation with a status code before any
+HIP call (so none of these tests needs a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fa.h")
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+F32, BF16 = 0, 1
+A = 1 << 20            # a fake, 16-byte aligned "device" address: never dereferenced
+MIS = A + 8            # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string",
+                 "fa_last_error", "fa_abi_version", "fa_decode_split_tokens"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(fa):
+    L = fa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(fa.SIGNATURES) == set(declared_functions())
+    assert L.fa_abi_version() == 1
+
+
+def test_status_strings(fa):
+    assert fa.status_string(FA_OK) == "ok"
+    assert "invalid" in fa.status_string(FA_ERR_INVALID)
+    assert "unsupported" in fa.status_string(FA_ERR_UNSUPPORTED)
+    assert "HIP" in fa.status_string(FA_ERR_HIP)
+
+
+def prefill(fa, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, causal=1, scale=0.125, dtype=BF16):
+    P = ctypes.c_void_p
+    return fa.lib().fa_prefill(P(q), P(k), P(v), P(o), P(lse), B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), FA_ERR_INVALID, "divide"),
+    (dict(Hq=0), FA_ERR_INVALID, "heads"),
+    (dict(B=-1), FA_ERR_INVALID, ">= 0"),
+    (dict(d=96), FA_ERR_UNSUPPORTED, "head dim"),
+    (dict(d=256), FA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=7), FA_ERR_INVALID, "dtype"),
+    (dict(causal=2), FA_ERR_INVALID, "causal"),
+    (dict(Nq=9, Nk=8), FA_ERR_INVALID, "Nq=9 > Nk=8"),
+    (dict(scale=0.0), FA_ERR_INVALID, "scale"),
+    (dict(scale=float("inf")), FA_ERR_INVALID, "scale"),
+    (dict(scale=float("nan")), FA_ERR_INVALID, "scale"),
+    (dict(q=0), FA_ERR_INVALID, "null"),
+    (dict(o=0), FA_ERR_INVALID, "null"),
+    (dict(k=MIS), FA_ERR_INVALID, "aligned"),
+    (dict(lse=MIS), FA_ERR_INVALID, "aligned"),
+])
+def test_prefill_rejects(fa, kw, status, msg):
+    assert prefill(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_prefill_empty_is_a_noop(fa):
+    # nothing is launched, so no GPU is needed and null pointers are fine
+    assert prefill(fa, q=0, k=0, v=0, o=0, lse=0, B=0) == FA_OK
+    assert prefill(fa, q=0, k=0, v=0, o=0, lse=0, Nq=0, Nk=0) == FA_OK
+    assert fa.lib().fa_last_error().decode() == ""
+
+
+def decode(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, o=A, lse=A,
+           B=2, Hq=8, Hkv=2, d=128, scale=0.1, dtype=BF16, split=0, ws=None, ws_bytes=0):
+    P = ctypes.c_void_p
+    return fa.lib().fa_decode(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, P(o), P(lse),
+                              B, Hq, Hkv, d, scale, dtype, split, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), FA_ERR_INVALID, "divide"),
+    (dict(d=80), FA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=5), FA_ERR_INVALID, "dtype"),
+    (dict(scale=-1.0), FA_ERR_INVALID, "scale"),
+    (dict(split=100), FA_ERR_INVALID, "multiple of 256"),
+    (dict(maxlen=-1), FA_ERR_INVALID, "max_seq_len"),
+    (dict(cap=32, maxlen=64), FA_ERR_INVALID, "capacity"),                 # contiguous S_cap < max len
+    (dict(table=A, bs=12), FA_ERR_INVALID, "power of two"),
+    (dict(table=A, bs=2048, mbps=1), FA_ERR_INVALID, "power of two"),
+    (dict(table=A, bs=16, mbps=3, maxlen=64), FA_ERR_INVALID, "max_blocks_per_seq"),
+    (dict(table=A, cap=0), FA_ERR_INVALID, "at least one block"),
+    (dict(q=0), FA_ERR_INVALID, "null"),
+    (dict(lens=0), FA_ERR_INVALID, "null"),
+    (dict(k=MIS), FA_ERR_INVALID, "aligned"),
+    (dict(lens=A + 2), FA_ERR_INVALID, "4-byte"),
+    (dict(table=A + 2), FA_ERR_INVALID, "4-byte"),
+    (dict(B=70000), FA_ERR_UNSUPPORTED, "grid"),
+])
+def test_decode_rejects(fa, kw, status, msg):
+    assert decode(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_decode_workspace_contract(fa):
+    L = fa.lib()
+    # one split per sequence needs no workspace
+    assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 256, 256) == 0
+    n = L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 256)
+    slots = 2 * 8 * 4
+    assert n == ((slots * 128 * 4 + 255) // 256) * 256 + ((slots * 4 + 255) // 256) * 256
+    # a call that needs it without one, or with too little, is rejected
+    assert decode(fa, maxlen=1024, cap=1024, split=256) == FA_ERR_INVALID
+    assert "workspace" in L.fa_last_error().decode()
+    assert decode(fa, maxlen=1024, cap=1024, split=256, ws=A, ws_bytes=n - 1) == FA_ERR_INVALID
+    assert decode(fa, maxlen=1024, cap=1024, split=256, ws=A + 16, ws_bytes=n) == FA_ERR_INVALID
+    # rejected sizes report 0
+    assert L.fa_decode_workspace_bytes(2, 8, 3, 128, 1024, 0) == 0
+
+
+def test_decode_split_choice(fa):
+    L = fa.lib()
+    for args in [(64, 32, 8, 128, 8192), (128, 32, 8, 128, 32768), (1, 32, 8, 128, 4096), (4, 8, 8, 64, 100)]:
+        st = L.fa_decode_split_tokens(*args)
+        assert st >= 256 and st % 256 == 0 and st <= 4096
+    assert L.fa_decode_split_tokens(2, 8, 3, 128, 100) == 0
+
+
+def test_decode_empty_batch_is_a_noop(fa):
+    assert decode(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, B=0) == FA_OK
+
+
+def test_no_cpu_fallback_without_gpu(fa):
+    """On a machine without a GPU the binding raises instead of computing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.prefill(q, q, q)
