@@ -32,8 +32,9 @@ namespace fa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kU = 4;          // token loads per wave per iteration
+constexpr int kU = 2;          // token loads per wave per pipeline stage
 constexpr int kElems = 16;     // elements of a row held by one lane
+constexpr float kSlack = 8.f;  // log2 units a running max may lag before rescaling
 
 template <typename T> struct Elem;
 template <> struct Elem<float> { static constexpr int kVecs = 4; };     // 16 floats = 4 x 16 B
@@ -90,6 +91,16 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Compiler-only fences (they emit no instruction): memory operations may not
+// move across the asm, and the machine scheduler may not move anything across
+// the sched_barrier.  Together they keep the prefetch loads of the next stage
+// ahead of the current stage's arithmetic; without them the loads are sunk next
+// to their first use and the pipeline collapses.
+__device__ __forceinline__ void keep_loads_here() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ int num_splits(int L, int max_seq_len, int chunk) {
   if (L < 0 || L > max_seq_len) return 1;  // invalid length: reported by split 0 as NaN
   return L <= chunk ? 1 : (L + chunk - 1) / chunk;
@@ -118,10 +129,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   __shared__ float red_ml[kWaves][QH][2];
   __shared__ int red_bad[kWaves];
 
-  const int s = blockIdx.x;
+  // grid: x = (KV head, query-head group) fastest, so the workgroups of all
+  // heads of one split are dispatched together and read the same pool blocks
+  // (each block interleaves the Hkv heads token by token); y = split; z = b.
+  const int s = blockIdx.y;
   const int nqg = (a.Hq / a.Hkv) / QH;
-  const int g = blockIdx.y / nqg;
-  const int h0 = g * (a.Hq / a.Hkv) + (blockIdx.y % nqg) * QH;
+  const int g = blockIdx.x / nqg;
+  const int h0 = g * (a.Hq / a.Hkv) + (blockIdx.x % nqg) * QH;
   const int b = blockIdx.z;
 
   const int L = a.seq_lens[b];
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   const int t_end = bad ? 0 : min(L, t_begin + a.split_tokens);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int grp = lane / G;
   const int sub = lane % G;
   const float c = a.scale * kLog2e;
@@ -162,55 +176,102 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   const int32_t* table = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
   const size_t contig_base = ((size_t)b * a.Hkv + g) * (size_t)a.kv_capacity;
 
-  for (int t0 = t_begin + wave * TOK_IT; t0 < t_end; t0 += kWaves * TOK_IT) {
-    u32x4_t kr[kU][NV], vr[kU][NV];
-    bool ok[kU];
+  // Two-stage software pipeline per wave.  Stage n: fetch the block-table
+  // entries of iteration n+2, issue the K/V loads of iteration n+1 (their
+  // table entries arrived during stage n-1), then compute iteration n.  Loads
+  // are never predicated: a lane past the end of the split reads the split's
+  // last (valid, finite) row and its score is masked to -inf, so its weight is
+  // exactly 0.  Program order keeps the K/V loads of n+1 in flight while
+  // iteration n is computed (vmcnt is counted in issue order).
+  const int stride = kWaves * TOK_IT;
+  struct Buf { u32x4_t k[kU][NV], v[kU][NV]; };
+
+  auto fetch_table = [&](int (&ph)[kU], int t0) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int tok = min(t0 + u * TPW + grp, t_end - 1);
+        ph[u] = table[tok >> a.log2_block_size];
+      }
+    }
+  };
+  auto issue = [&](Buf& B, int t0, const int (&ph)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int tok = t0 + u * TPW + grp;
-      ok[u] = tok < t_end;
-      size_t row = 0;
-      if (ok[u]) {
-        if constexpr (PAGED) {
-          int phys = table[tok >> a.log2_block_size];
-          if (phys < 0 || phys >= a.kv_capacity) { bad = true; phys = 0; }
-          row = ((size_t)phys * a.block_size + (tok & (a.block_size - 1))) * a.Hkv + g;
-        } else {
-          row = contig_base + tok;
-        }
+      const int tok = min(t0 + u * TPW + grp, t_end - 1);
+      size_t row;
+      if constexpr (PAGED) {
+        int phys = ph[u];
+        if (phys < 0 || phys >= a.kv_capacity) { bad = true; phys = 0; }
+        row = ((size_t)phys * a.block_size + (tok & (a.block_size - 1))) * a.Hkv + g;
+      } else {
+        row = contig_base + tok;
       }
       const size_t base = row * row_vecs + sub;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        kr[u][j] = ok[u] ? kbase[base + j * G] : u32x4_t{0, 0, 0, 0};
-        vr[u][j] = ok[u] ? vbase[base + j * G] : u32x4_t{0, 0, 0, 0};
+        B.k[u][j] = kbase[base + j * G];
+        B.v[u][j] = vbase[base + j * G];
       }
     }
+  };
+  auto compute = [&](const Buf& B, int t0) {
 #pragma unroll
     for (int r = 0; r < QH; ++r) {
       float sc[kU];
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const float part = dot16(q[r], kr[u], T{});
-        sc[u] = ok[u] ? group_sum<G>(part) * c : -INFINITY;
+        const float part = group_sum<G>(dot16(q[r], B.k[u], T{}));
+        sc[u] = (t0 + u * TPW + grp < t_end) ? part * c : -INFINITY;
         mx = fmaxf(mx, sc[u]);
       }
+      // Rescale only when some lane's max grows by more than kSlack: the
+      // state (m, l, o) stays exact for any reference m >= the true max - kSlack,
+      // the weights are then at most 2^kSlack, and most stages skip the multiply.
       const float mn = fmaxf(m[r], mx);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(m[r] - mu);
+      if (__any(mn > m[r] + kSlack)) {
+        const float alpha = fast_exp2(m[r] - ((mn == -INFINITY) ? 0.f : mn));
+        l[r] *= alpha;
+#pragma unroll
+        for (int i = 0; i < kElems; ++i) o[r][i] *= alpha;
+        m[r] = mn;
+      }
+      const float mu = (m[r] == -INFINITY) ? 0.f : m[r];
       float psum = 0.f;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         sc[u] = fast_exp2(sc[u] - mu);
         psum += sc[u];
       }
-      l[r] = l[r] * alpha + psum;
+      l[r] += psum;
 #pragma unroll
-      for (int i = 0; i < kElems; ++i) o[r][i] *= alpha;
-#pragma unroll
-      for (int u = 0; u < kU; ++u) axpy16(o[r], sc[u], vr[u], T{});
-      m[r] = mn;
+      for (int u = 0; u < kU; ++u) axpy16(o[r], sc[u], B.v[u], T{});
+    }
+  };
+
+  int t0 = t_begin + wave * TOK_IT;
+  if (t0 < t_end) {
+    Buf A, Bb;
+    int pA[kU], pB[kU];
+    fetch_table(pA, t0);
+    fetch_table(pB, t0 + stride);
+    issue(A, t0, pA);
+    // No branch around the prefetch: past the end of the split every lane's
+    // token is clamped to the split's last row, so the one surplus stage per
+    // wave re-reads a single cached row.
+    for (;;) {
+      fetch_table(pA, t0 + 2 * stride);
+      issue(Bb, t0 + stride, pB);
+      keep_loads_here();
+      compute(A, t0);
+      if (t0 + stride >= t_end) break;
+      fetch_table(pB, t0 + 3 * stride);
+      issue(A, t0 + 2 * stride, pA);
+      keep_loads_here();
+      compute(Bb, t0 + stride);
+      if (t0 + 2 * stride >= t_end) break;
+      t0 += 2 * stride;
     }
   }
 
@@ -299,7 +360,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D, int QH>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
   const int nqg = (a.Hq / a.Hkv) / QH;
-  dim3 grid(a.max_splits, a.Hkv * nqg, a.B);
+  dim3 grid(a.Hkv * nqg, a.max_splits, a.B);
   if (a.block_table)
     hipLaunchKernelGGL((decode_split_kernel<T, D, QH, true>), grid, dim3(kWaves * 64), 0, st, a);
   else

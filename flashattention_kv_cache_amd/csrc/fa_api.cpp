@@ -38,15 +38,15 @@ int ilog2(int x) {
 }
 
 // Tokens per decode split when the caller leaves the choice to the library:
-// aim for about 8192 splits over (sequence, KV head group) pairs if every
-// sequence had max_seq_len tokens, with at least 256 and at most 4096 tokens
+// aim for about 16384 splits over (sequence, KV head group) pairs if every
+// sequence had max_seq_len tokens, with at least 512 and at most 4096 tokens
 // per split (a power of two).
 int choose_split_tokens(int B, int Hq, int Hkv, int max_seq_len) {
   const int n_rep = Hq / Hkv;
   const int qh = n_rep % 8 == 0 ? 8 : n_rep % 4 == 0 ? 4 : n_rep % 2 == 0 ? 2 : 1;
   const double pairs = (double)B * Hkv * (n_rep / qh);
-  double want = pairs * (double)max_seq_len / 8192.0;
-  int st = 256;
+  double want = pairs * (double)max_seq_len / 16384.0;
+  int st = 512;
   while (st < 4096 && st * 2 <= want) st *= 2;
   return st;
 }
@@ -166,7 +166,8 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
       return fail(FA_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID, "workspace must be 256-byte aligned");
   }
-  if (B > 65535 || Hq > 65535) return fail(FA_ERR_UNSUPPORTED, "grid too large (B and Hq must be <= 65535)");
+  if (B > 65535 || Hq > 65535 || ns > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (B, Hq and the number of splits must be <= 65535)");
 
   fa::DecodeArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.block_table = block_table;

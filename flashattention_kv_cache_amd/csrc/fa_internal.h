@@ -102,6 +102,9 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
   return r;
 }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum, i.e. not waited).
+__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
