@@ -29,6 +29,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill": ["flashattention_kv_cache_amd/csrc/prefill_bf16.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
+    "decode": ["flashattention_kv_cache_amd/csrc/decode.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
+}
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "prefill TFLOP/s & decode KV GB/s (% of MI355X peak), GQA d=128 bf16"
 
@@ -43,6 +48,29 @@ def parse():
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run one device copy of this many MiB (a known-size kernel for HBM counters)")
     return p.parse_args()
+
+
+def source_sha(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (already scaled by the copy-kernel calibration), or None when the
+    kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kind):
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -192,10 +220,11 @@ def main():
         "decode": {"value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(dec_avg, 5),
                    "kernel_ms_median": round(dec_ms[K // 2], 5), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_bf16_kernel<128>"},
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill"),
+                     "algorithmic_bytes": wp.algorithmic_bytes(), "kernel": "prefill_bf16_kernel<128>"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
+                            "algorithmic_bytes": dec_bytes,
                             "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
         "wall_s_timed": round(wall, 4),
     }

@@ -13,7 +13,9 @@
 // gfx950 mapping (not from the pages):
 //   * workgroup = 4 waves = 128 query rows; each wave owns 32 rows.  Key and
 //     value tiles of 64 rows go from HBM straight into LDS with
-//     global_load_lds_dwordx4 (no staging registers, no vector ALU work):
+//     global_load_lds_dwordx4 (no staging registers, no vector ALU work),
+//     issued from inline assembly so that nothing waits for them before the
+//     end of the tile they overlap:
 //     K and V each double buffered, staggered by one tile.
 //   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     A = 32 keys x 16 dims from LDS, B = 16 dims x 32 queries kept in
@@ -28,13 +30,13 @@
 //     tile with two ds_read_b64_tr_b16 (each gives a lane 4 keys of its
 //     dimension); the rows they address follow the same permutation.
 //   * LDS tiles are XOR-swizzled in 16-byte chunks (the swizzle is applied to
-//     the source addresses of the direct loads): K by row % 8, so 16-byte
-//     operand reads of 8 consecutive keys hit distinct banks; V by
-//     2 * (row % 4), so each transposed read of 4 keys x 16 dims does.
-//   * software pipeline inside each wave: iteration t runs the QK^T MFMAs of
-//     tile t+1 interleaved with the softmax arithmetic of tile t (they are
-//     independent), then the PV MFMAs of tile t; the direct loads of K(t+2)
-//     and V(t+1) fly during the whole iteration.  One barrier per tile.
+//     the source addresses of the direct loads) so that both the 16-byte K
+//     operand reads and the transposed V reads are free of bank conflicts.
+//   * software pipeline inside each wave: stage t runs the QK^T MFMAs of tile
+//     t+1 and the PV MFMAs of tile t-1 interleaved with the softmax arithmetic
+//     of tile t (all three are independent), so each wave keeps its matrix
+//     cores fed while its vector ALUs work; the direct loads of K(t+2) and
+//     V(t) fly during the whole stage.  One barrier per tile.
 //   * causal: only key tiles left of and on the diagonal are visited, the mask
 //     is evaluated only on tiles that cross the diagonal or the key tail, and
 //     the grid is ordered longest query tiles first; workgroups that share a
@@ -63,30 +65,84 @@ struct Smem {
   uint16_t v[2][kBN * D];  // row-major V tiles, chunks swizzled by 2 * (row % 4)
 };
 
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+// Forces a value to be computed at this point of the program (an empty asm
+// that reads it; no instruction is emitted).  Used so that the softmax of a
+// tile is not sunk past the barrier into the next stage, where it could no
+// longer overlap this stage's MFMAs.
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(const u32x4_t& x) { asm volatile("" ::"v"(x)); }
 
-// Direct global -> LDS copy of tile rows [key0, key0 + 64) of one head.  A
-// wave instruction writes 1 KiB of consecutive LDS (lane L at 16 L); lane L
-// fetches the global chunk that the swizzle places there.  Rows at or past Nk
-// are read from row Nk - 1 instead: harmless (keys >= Nk get weight 0 and the
-// clamped V rows are finite) and never out of bounds.  Tiles past the last
-// one are loaded the same way and never used.
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst_tile, int key0, int Nk, int wave, int lane) {
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;         // rows per wave instruction
-  constexpr int IPW = kBN / RPI / 4;    // instructions per wave
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int row = (wave * IPW + i) * RPI + lane / CPR;
-    const int p = lane % CPR;
-    const int c = p ^ (IS_V ? v_swz(row) : k_swz(row));
-    const int key = min(key0 + row, Nk - 1);
-    lds_u16* dst = (lds_u16*)(dst_tile + (wave * IPW + i) * RPI * D);
-    __builtin_amdgcn_global_load_lds(src + (size_t)key * D + c * 8, dst, 16, 0, 0);
-  }
+// The LDS has 64 banks of 4 bytes: a 16-byte read is served 16 lanes per
+// cycle, an 8-byte read 32 lanes per cycle.  Swizzles are XOR masks on the
+// 16-byte chunk index of a row.
+//   K operand reads: 16 lanes read 16 consecutive rows at one logical chunk.
+//     d=128 (16 chunks per 256-byte row): mask = row % 16.
+//     d=64 (8 chunks per 128-byte row, two rows per bank line): mask = (row/2) % 8.
+//   V transposed reads: 32 lanes read rows 4i..4i+3 at 4 consecutive chunks.
+//     d=128: mask = 4 (row % 4);  d=64: mask = 4 ((row/2) % 2).
+template <int D> __device__ __forceinline__ int k_swz(int row) { return (row / (128 / D)) & (D / 8 - 1); }
+template <int D> __device__ __forceinline__ int v_swz(int row) { return ((row / (128 / D)) & (D / 32 - 1)) << 2; }
+
+// Direct global -> LDS copies (global_load_lds_dwordx4).  A wave instruction
+// writes 1 KiB of consecutive LDS starting at M0 (lane L at 16 L); lane L
+// fetches the global chunk that the swizzle places there.
+//
+// They are issued from inline assembly on purpose: the compiler cannot tell
+// which LDS bytes such a load writes, and would otherwise drain every one of
+// them (s_waitcnt vmcnt(0)) before the next transposed LDS read, i.e. in the
+// middle of the tile that overlaps them.  The instruction writes no VGPR, so
+// no register can be reused under it; the kernel itself waits for all of
+// them (wait_all_vmem) before the barrier that publishes the tile, and
+// vector-memory loads retire in order, so the compiler's own waits for other
+// loads stay correct (only stricter).  M0 is written in the same block and
+// declared clobbered; s_nop 0 covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma_saddr(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+__device__ __forceinline__ void lds_dma_vaddr(const void* vaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(vaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Per-lane layout of one tile copy: instruction i of this wave fills LDS rows
+// (wave * IPW + i) * RPI .. + RPI - 1 of the tile.
+template <int D, bool IS_V>
+struct TileCopy {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows per wave instruction
+  static constexpr int IPW = kBN / RPI / 4;  // instructions per wave
+  uint32_t off[IPW];                         // byte offset of this lane's chunk within the tile
+
+  __device__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = (wave * IPW + i) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+      off[i] = (uint32_t)((row * D + c * 8) * 2);
+    }
+  }
+  // Rows [key0, key0 + 64) of one head (src = row 0 of the head) into dst.
+  // Rows at or past Nk are read from row Nk - 1 (harmless: those keys get
+  // weight 0 and the clamped V rows are finite; never out of bounds).
+  __device__ __forceinline__ void copy(const uint16_t* src, const uint16_t* dst_tile, int key0, int Nk, int wave,
+                                       int lane) const {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u16*)dst_tile + (uint32_t)(wave * IPW * RPI * D * 2);
+    if (key0 + kBN <= Nk) {
+      const uint16_t* base = src + (size_t)key0 * D;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) lds_dma_saddr(off[i], base, lds0 + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int row = (wave * IPW + i) * RPI + lane / CPR;
+        const int key = min(key0 + row, Nk - 1);
+        const int c = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+        lds_dma_vaddr(src + (size_t)key * D + c * 8, lds0 + i * 1024);
+      }
+    }
+  }
+};
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb) {
@@ -148,11 +204,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   float m = -INFINITY, l0 = 0.f, l1 = 0.f;
   const float c = a.scale * kLog2e;
 
+  TileCopy<D, false> kcp;
+  TileCopy<D, true> vcp;
+  kcp.init(wave, lane);
+  vcp.init(wave, lane);
+
   // LDS element offset of this lane's K operand (row kb*32 + col, logical
   // 16-byte chunk ks*2 + hl), and of its V^T transposed reads.
   auto k_off = [&](int kb, int ks) {
     const int row = kb * 32 + col;
-    return row * D + (((ks * 2 + hl) ^ k_swz(row)) * 8);
+    return row * D + (((ks * 2 + hl) ^ k_swz<D>(row)) * 8);
   };
   // V^T operand for k-step kk (keys 16kk .. 16kk+15) and dims db*32 .. +31:
   // lane L of 16-lane group gi reads row key(j) = 16kk + 8*half + 4*(gi/2) + j
@@ -162,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   auto v_off = [&](int kk, int half, int db) {
     const int row = kk * 16 + half * 8 + (gi >> 1) * 4 + (li >> 2);
     const int d = db * 32 + (gi & 1) * 16 + (li & 3) * 4;
-    return row * D + ((((d >> 3) ^ v_swz(row)) << 3) | (d & 7));
+    return row * D + ((((d >> 3) ^ v_swz<D>(row)) << 3) | (d & 7));
   };
 
   // S^T of one tile for this wave's 32 queries: two 32-key blocks
@@ -188,14 +249,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
         if (kb * 32 + (r / 4) * 8 + (r % 4) > lim) sacc[kb][r] = -INFINITY;
   };
 
-  // One pipeline stage: softmax + PV of tile t (scores in sc), QK^T of tile
-  // t+1 into sn, direct loads of K(t+2) and V(t+1) in flight.
-  auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], int t) {
-    const int cb = t & 1;  // buffer holding V(t); K(t+1) sits in cb ^ 1
-    dma_tile<D, false>(kg, sm.k[cb], (t + 2) * kBN, a.Nk, wave, lane);
-    dma_tile<D, true>(vg, sm.v[cb ^ 1], (t + 1) * kBN, a.Nk, wave, lane);
+  bool pending = false;  // wave-uniform: a rescale of O is due
+  float pend_alpha = 1.f;
 
-    // ---- part A: mask, running max, rare rescale
+  // O^T += V(t)^T P(t) for the V tile in buffer vb (16 MFMAs).
+  auto pv = [&](const bf16x8_t (&pp)[4], int vb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[vb] + v_off(kk, 0, db)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[vb] + v_off(kk, 1, db)));
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[kk], oacc[db], 0, 0, 0);
+      }
+  };
+
+  // One pipeline stage t: softmax of tile t (scores in sc, weights out to pc)
+  // on the vector ALUs, while the matrix cores run QK^T of tile t+1 (into sn)
+  // and PV of tile t-1 (weights pp, V in buffer (t-1)&1).  The direct loads
+  // of K(t+2) and V(t) fly during the whole stage.
+  auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
+                   bool with_pv) {
+    const int kb_next = (t + 1) & 1;  // K(t+1)
+    if (t + 2 < n_tiles) kcp.copy(kg, sm.k[t & 1], (t + 2) * kBN, a.Nk, wave, lane);
+    vcp.copy(vg, sm.v[t & 1], t * kBN, a.Nk, wave, lane);
+
+    // A rescale decided in the previous stage applies to O once PV(t-2) (its
+    // weights used the old reference) is in, i.e. now, before PV(t-1) starts.
+    if (pending) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
+      pending = false;
+    }
+
+    // ---- running max of tile t; a rescale it calls for applies to l now and
+    // to O at the start of the next stage, after PV(t-1).
     if (t >= n_clean) mask(sc, t);
     float mx = sc[0][0];
 #pragma unroll
@@ -208,71 +299,89 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     // true max, and P is then at most 2^kSlack (fine in bf16).
     const float mn = fmaxf(m, mx);
     if (__any(mn > m + kSlack)) {
-      const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
-      l0 *= alpha;
-      l1 *= alpha;
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      pend_alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
+      pending = true;
+      l0 *= pend_alpha;
+      l1 *= pend_alpha;
       m = mn;
     }
     const float mu = (m == -INFINITY) ? 0.f : m;
 
-    // ---- part B: S(t+1) on the matrix cores, P(t) on the vector ALUs
-    bf16x8_t pf[4];
+    // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.k[cb ^ 1][k_off(kb, ks)]);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(kb, ks)]);
         sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sn[kb], 0, 0, 0);
+        if (with_pv) {
+          // PV(t-1) has 4 * DB = 2 * KS MFMAs, as many as QK^T: one per k-step.
+          const int j = kb * KS + ks;
+          const int kk = j / DB, db = j % DB;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[kk], oacc[db], 0, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < VPS; ++j) {
           const int r = ks * VPS + j;
           p[r] = fast_exp2(fmaf(sc[kb][r], c, -mu));
           if (j & 1) l1 += p[r]; else l0 += p[r];
         }
+        // interleave: LDS operand reads, the two MFMAs, then vector work
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU incl. transcendental
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4_t w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[half * 8 + 2 * i], p[half * 8 + 2 * i + 1]);
-        pf[kb * 2 + half] = __builtin_bit_cast(bf16x8_t, w);
+        pin(w);
+        pc[kb * 2 + half] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
-
-    // ---- part C: O^T += V(t)^T P(t)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[cb] + v_off(kk, 0, db)));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[cb] + v_off(kk, 1, db)));
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kk], oacc[db], 0, 0, 0);
-      }
+    pin(l0);
+    pin(l1);
     wait_all_vmem();  // this wave's direct loads have landed
     __syncthreads();  // ... and every other wave's
   };
 
   f32x16_t s_a[2], s_b[2];
+  bf16x8_t p_a[4], p_b[4];
+
+  // prologue: K(0) -> K buffer 0, K(1) -> K buffer 1.  The drain is
+  // unconditional so that, on every path into the loop, the Q fragments are
+  // known to have arrived (otherwise each QK^T MFMA waits on vmcnt).
   if (n_tiles > 0) {
-    // prologue: K(0), V(0) -> buffer 0, K(1) -> K buffer 1
-    dma_tile<D, false>(kg, sm.k[0], 0, a.Nk, wave, lane);
-    dma_tile<D, true>(vg, sm.v[0], 0, a.Nk, wave, lane);
-    dma_tile<D, false>(kg, sm.k[1], kBN, a.Nk, wave, lane);
-    wait_all_vmem();
-    __syncthreads();
-    qk(s_a, 0);
-    __syncthreads();  // K buffer 0 is refilled by the first stage
+    kcp.copy(kg, sm.k[0], 0, a.Nk, wave, lane);
+    if (n_tiles > 1) kcp.copy(kg, sm.k[1], kBN, a.Nk, wave, lane);
   }
-  for (int t = 0; t < n_tiles; t += 2) {
-    stage(s_a, s_b, t);
-    if (t + 1 >= n_tiles) break;
-    stage(s_b, s_a, t + 1);
+  wait_all_vmem();
+  __syncthreads();
+  if (n_tiles > 0) qk(s_a, 0);
+  __syncthreads();  // K buffer 0 is refilled by the first stage
+
+  if (n_tiles > 0) {
+    stage(s_a, s_b, p_b, p_a, 0, false);
+    int t = 1;
+    for (; t + 1 < n_tiles; t += 2) {
+      stage(s_b, s_a, p_a, p_b, t, true);
+      stage(s_a, s_b, p_b, p_a, t + 1, true);
+    }
+    if (t < n_tiles) stage(s_b, s_a, p_a, p_b, t, true);
+    // drain: a due rescale, then PV of the last tile
+    if (pending) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
+    }
+    if (t < n_tiles) pv(p_b, t & 1);
+    else pv(p_a, (t - 1) & 1);
   }
 
   // ---- epilogue: one division, bf16 output, natural-log LSE
