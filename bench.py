@@ -41,8 +41,10 @@ METRIC = "prefill TFLOP/s & decode KV GB/s (% of MI355X peak), GQA d=128 bf16"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    # ~0.4 s of untimed work: the GPU clock ramps up over the first few
+    # hundred milliseconds of load, and prefill throughput follows it.
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-tokens", type=int, default=0, help="decode tokens per split (0 = library choice)")
     p.add_argument("--copy-calib-mib", type=int, default=0,

@@ -17,6 +17,9 @@
 //   * a token row (d elements) is read by G = d/16 lanes, 16 elements each, as
 //     16-byte loads; a wave covers 64/G tokens per load and issues U such loads
 //     for K and for V before using any of them;
+//   * bf16: q.k with v_dot2_f32_bf16; the weighted sum of V pairs the two
+//     tokens a lane holds per stage and uses v_dot2 as well (the weights go to
+//     bf16 there, as in prefill; the row sum stays fp32);
 //   * scores are reduced across the G lanes with DPP, and each G-lane group
 //     keeps its own running (max, sum, output) — the recurrence of the "Li
 //     Hongyi, Machine Learning 2026" notes, lecture "FlashAttention" — so the
@@ -216,6 +219,18 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
     }
   };
   auto compute = [&](const Buf& B, int t0) {
+    // bf16: element i of the two tokens of this stage, paired for v_dot2
+    uint32_t vpair[kElems];
+    if constexpr (sizeof(T) == 2) {
+      static_assert(kU == 2, "v_dot2 pairs the two token loads of a stage");
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          vpair[j * 8 + 2 * t] = __builtin_amdgcn_perm(B.v[1][j][t], B.v[0][j][t], 0x05040100u);
+          vpair[j * 8 + 2 * t + 1] = __builtin_amdgcn_perm(B.v[1][j][t], B.v[0][j][t], 0x07060302u);
+        }
+    }
 #pragma unroll
     for (int r = 0; r < QH; ++r) {
       float sc[kU];
@@ -245,8 +260,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
         psum += sc[u];
       }
       l[r] += psum;
+      if constexpr (sizeof(T) == 2) {
+        // o += p0 V0 + p1 V1 for all 16 elements with one v_dot2 each
+        const bf16x2_t pw = as_bf16x2(pack_bf16x2(sc[0], sc[1]));
 #pragma unroll
-      for (int u = 0; u < kU; ++u) axpy16(o[r], sc[u], B.v[u], T{});
+        for (int i = 0; i < kElems; ++i)
+          o[r][i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vpair[i]), pw, o[r][i], false);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) axpy16(o[r], sc[u], B.v[u], T{});
+      }
     }
   };
 
