@@ -211,6 +211,90 @@ def make_decode_inputs(B, Hq, Hkv, d, dtype, seed, len_range=None, seq_lens=None
     return DecodeInputs(q, k, v, seq_lens.to(torch.int32), table, bs, total, max_seq_len)
 
 
+@dataclass
+class ChunkedInputs:
+    """A chunk of n new tokens per sequence, to be appended to a KV cache that
+    already holds each sequence's past, then attended causally against the
+    whole sequence."""
+    q: torch.Tensor                 # (B, Hq, n, d)
+    k_new: torch.Tensor             # (B, Hkv, n, d)
+    v_new: torch.Tensor
+    k_cache: torch.Tensor           # contiguous (B, Hkv, S_cap, d) or pool (nb, bs, Hkv, d); past only
+    v_cache: torch.Tensor
+    seq_lens: torch.Tensor          # (B,) int32: past + n, the lengths after the append
+    block_table: Optional[torch.Tensor]
+    block_size: int
+    kv_capacity: int
+    max_seq_len: int
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+
+def make_chunked_inputs(B, Hq, Hkv, d, dtype, seed, chunk, past_range=None, past_lens=None,
+                        paged=True, block_size=16, s_cap: Optional[int] = None,
+                        max_blocks: Optional[int] = None, spare_blocks: int = 0,
+                        shared_prefix_blocks: int = 0) -> ChunkedInputs:
+    """Give ``past_range=(lo, hi)`` (past lengths drawn uniformly, inclusive) or
+    ``past_lens``.  The cache holds the past tokens; the slots the chunk will
+    occupy, like every other slot no sequence owns, hold NaN until the append.
+    ``shared_prefix_blocks`` makes sequences 1.. list the first blocks of
+    sequence 0 as their own first blocks (a shared prompt)."""
+    g = torch.Generator().manual_seed(seed)
+    if past_lens is None:
+        lo, hi = past_range
+        past = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64)
+        max_seq_len = hi + chunk
+    else:
+        past = torch.tensor(list(past_lens), dtype=torch.int64)
+        max_seq_len = (int(past.max()) if B > 0 else 0) + chunk
+    lens = past + chunk
+    q = _normal(g, (B, Hq, chunk, d), dtype)
+    k_new = _normal(g, (B, Hkv, chunk, d), dtype)
+    v_new = _normal(g, (B, Hkv, chunk, d), dtype)
+    if not paged:
+        cap = s_cap if s_cap is not None else max_seq_len
+        k = _normal(g, (B, Hkv, cap, d), dtype)
+        v = _normal(g, (B, Hkv, cap, d), dtype)
+        for b in range(B):
+            k[b, :, int(past[b]):] = float("nan")
+            v[b, :, int(past[b]):] = float("nan")
+        return ChunkedInputs(q, k_new, v_new, k, v, lens.to(torch.int32), None, 0, cap, max_seq_len)
+    bs = block_size
+    sp = shared_prefix_blocks
+    if sp and any(int(p) < sp * bs for p in past):
+        raise ValueError("every past must cover the shared prefix blocks")
+    nblk = [(int(L) + bs - 1) // bs for L in lens]
+    owned = [n - (sp if b > 0 else 0) for b, n in enumerate(nblk)]
+    total = sum(owned) + spare_blocks
+    perm = torch.randperm(total, generator=g)
+    mb = max_blocks if max_blocks is not None else max(1, (max_seq_len + bs - 1) // bs)
+    table = torch.full((B, mb), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        own = perm[off:off + owned[b]].to(torch.int32)
+        off += owned[b]
+        if b > 0 and sp:
+            table[b, :sp] = table[0, :sp]
+            table[b, sp:nblk[b]] = own
+        else:
+            table[b, :nblk[b]] = own
+    k = _normal(g, (total, bs, Hkv, d), dtype)
+    v = _normal(g, (total, bs, Hkv, d), dtype)
+    for b in range(B):                       # chunk slots and the unused tail: NaN
+        P = int(past[b])
+        for j in range(P // bs, nblk[b]):
+            blk = int(table[b, j])
+            s0 = P % bs if j == P // bs else 0
+            k[blk, s0:] = float("nan")
+            v[blk, s0:] = float("nan")
+    for p in perm[sum(owned):].tolist():
+        k[p] = float("nan")
+        v[p] = float("nan")
+    return ChunkedInputs(q, k_new, v_new, k, v, lens.to(torch.int32), table, bs, total, max_seq_len)
+
+
 # The five workloads: seeds are 1000 + index.  Head layouts follow the pages'
 # examples: 32 query / 8 KV heads of width 128 (Llama 3 8B style) and 64 / 8
 # (Llama 3 70B style); paged blocks of 16 tokens.

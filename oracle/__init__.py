@@ -14,6 +14,9 @@ Modules:
              earlier partials) and the merge of two partial states; used to pin
              the definition, never to produce expected values for kernels.
   kv_bytes   the KV-cache size formula.
+  paged      the paged pool: free-list block allocation, token append through
+             the block table, prefix sharing, and chunked prefill (the newest
+             Nq tokens of each sequence against its whole cache).
 
 Every function cites the passage it follows by page title and section.  All
 functions are pinned by tests that check them against values the pages print,
@@ -23,10 +26,14 @@ from .attention import (kv_head_of, causal_key_limit, attention_rows, prefill,
                         prefill_rows, paged_gather, decode_contiguous, decode_paged)
 from .online import online_softmax_stats, online_attention_row, merge_partials
 from .kv_bytes import kv_cache_bytes, kv_bytes_per_token
+from .paged import (BlockAllocator, PagedSequence, append_token, share_prefix, append_batch,
+                    append_batch_contiguous, chunked_prefill)
 
 __all__ = [
     "kv_head_of", "causal_key_limit", "attention_rows", "prefill", "prefill_rows",
     "paged_gather", "decode_contiguous", "decode_paged",
     "online_softmax_stats", "online_attention_row", "merge_partials",
     "kv_cache_bytes", "kv_bytes_per_token",
+    "BlockAllocator", "PagedSequence", "append_token", "share_prefix", "append_batch",
+    "append_batch_contiguous", "chunked_prefill",
 ]
