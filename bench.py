@@ -15,6 +15,8 @@ Printed: one JSON line.  ``value`` is prefill TFLOP/s (algorithmic flops:
 object holds the decode KV GB/s (algorithmic bytes: every cached K/V byte once,
 plus q, o, lse and the block-table entries read).  Kernel durations come from
 HIP events recorded around each launch on the stream the kernels run on.
+``extras`` (outside the step, skipped with --no-extras) times the KV append
+and the chunked prefill against a paged cache on their own.
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def parse():
     p.add_argument("--split-tokens", type=int, default=0, help="decode tokens per split (0 = library choice)")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run one device copy of this many MiB (a known-size kernel for HBM counters)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the measurements outside the step (KV append, chunked prefill)")
     return p.parse_args()
 
 
@@ -73,6 +77,70 @@ def measured_traffic(kind: str):
     if rec.get("source_sha") != source_sha(kind):
         return None
     return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Average and median kernel time (ms) of fn() over `steps` launches, from
+    HIP events recorded around each launch on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return sum(ms) / steps, ms[steps // 2]
+
+
+def extras(dev, steps: int):
+    """The KV append and the chunked prefill against a paged cache, each on its
+    own: 1024-token chunks of 4 sequences appended to paged caches holding
+    1024..7168 tokens, then attended causally against the whole sequences."""
+    import torch
+    from flashattention_kv_cache_amd import binding
+    from flashattention_kv_cache_amd import workloads as W
+    w = W.CHUNKED
+    ci = W.chunked_inputs(w)
+    q, kn, vn = ci.q.to(dev), ci.k_new.to(dev), ci.v_new.to(dev)
+    kc, vc = ci.k_cache.to(dev), ci.v_cache.to(dev)
+    lens, table = ci.seq_lens.to(dev), ci.block_table.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def append():
+        binding.kv_append(kn, vn, kc, vc, lens, block_table=table)
+
+    def chunk():
+        binding.chunked_prefill(q, kc, vc, lens, block_table=table, max_seq_len=ci.max_seq_len,
+                                scale=w.scale, out=o, lse=lse)
+
+    append()
+    a_avg, a_med = time_launches(append, steps, 20)
+    c_avg, c_med = time_launches(chunk, steps, 50)
+    flops = w.flops(ci.seq_lens.tolist())
+    # new K/V read and written once, plus seq_lens and the table entries of the written blocks
+    ents = sum((int(L) + w.block_size - 1) // w.block_size - (int(L) - w.chunk) // w.block_size
+               for L in ci.seq_lens.tolist())
+    abytes = w.append_bytes() + w.B * 4 + ents * 4
+    tf = flops / (c_avg * 1e-3) / 1e12
+    gbs = abytes / (a_avg * 1e-3) / 1e9
+    return {
+        "chunked_prefill": {"workload": w.name, "value": round(tf, 3), "unit": "TFLOP/s",
+                            "kernel_ms": round(c_avg, 5), "kernel_ms_median": round(c_med, 5), "flops": flops,
+                            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                         "kernel": "prefill_bf16_kernel<128, paged>"}},
+        "kv_append": {"workload": f"append of the same chunks ({w.B} x {w.chunk} tokens, {w.Hkv} KV heads, "
+                                  f"d={w.d}, bf16) into the paged pool",
+                      "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(a_avg, 5),
+                      "kernel_ms_median": round(a_med, 5), "bytes": abytes,
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "kv_append_kernel"}},
+    }
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -223,13 +291,15 @@ def main():
                    "kernel_ms_median": round(dec_ms[K // 2], 5), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill"),
-                     "algorithmic_bytes": wp.algorithmic_bytes(), "kernel": "prefill_bf16_kernel<128>"},
+                     "algorithmic_bytes": wp.algorithmic_bytes(), "kernel": "prefill_bf16_kernel<128, contiguous>"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                             "algorithmic_bytes": dec_bytes,
                             "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_extras:
+        out["extras"] = extras(dev, max(10, min(K, 50)))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

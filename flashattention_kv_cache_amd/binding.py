@@ -28,6 +28,8 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _S),
     "fa_decode_split_tokens": ([_I, _I, _I, _I, _I], _I),
     "fa_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P], _I),
+    "fa_kv_append": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P], _I),
+    "fa_chunked_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -112,6 +114,87 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
     return out, lse
 
 
+class _Cache:
+    """Layout of a KV cache as the C ABI takes it."""
+
+    def __init__(self, Hkv, paged, block_size, capacity, max_blocks, bound):
+        self.Hkv, self.paged, self.block_size = Hkv, paged, block_size
+        self.capacity, self.max_blocks, self.bound = capacity, max_blocks, bound
+
+
+def _cache_layout(ref, k_cache, v_cache, seq_lens, block_table, block_size, B, d) -> _Cache:
+    """Check a contiguous cache (B, Hkv, S_cap, d) or a paged pool
+    (num_blocks, block_size, Hkv, d) with its block table (B, max_blocks)."""
+    for t, n in ((ref, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 with one entry per sequence")
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be 4-d")
+    if block_table is not None:
+        _dev(block_table, "block_table")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 (B, max_blocks)")
+        nblk, bs, Hkv, dk = k_cache.shape
+        if block_size and block_size != bs:
+            raise ValueError("block_size disagrees with the pool shape")
+        c = _Cache(Hkv, True, bs, nblk, block_table.shape[1], block_table.shape[1] * bs)
+    else:
+        Bc, Hkv, cap, dk = k_cache.shape
+        if Bc != B:
+            raise ValueError("cache batch != q batch")
+        c = _Cache(Hkv, False, 0, cap, 0, cap)
+    if dk != d or v_cache.shape != k_cache.shape or k_cache.dtype != ref.dtype or v_cache.dtype != ref.dtype:
+        raise ValueError("inputs and caches disagree in head dim, shape or dtype")
+    return c
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None, block_size: int = 0,
+              stream=None) -> None:
+    """fa_kv_append: write k_new/v_new (B, Hkv, n_new, d) into the cache at
+    positions seq_lens[b] - n_new .. seq_lens[b] - 1 (seq_lens = lengths after
+    the append), in place."""
+    _dev(v_new, "v_new")
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("expected k_new, v_new (B, Hkv, n_new, d) of one dtype")
+    B, Hkv, n_new, d = k_new.shape
+    c = _cache_layout(k_new, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
+    if c.Hkv != Hkv:
+        raise ValueError("new rows and cache disagree in KV heads")
+    _check(lib().fa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                              _ptr(block_table), c.block_size, c.max_blocks, c.capacity,
+                              B, Hkv, n_new, d, _dtype_code(k_new), _stream(stream)))
+
+
+def chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                    block_table: Optional[torch.Tensor] = None, block_size: int = 0,
+                    max_seq_len: Optional[int] = None, causal: bool = True, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fa_chunked_prefill: the Nq newest tokens of each sequence, q
+    (B, Hq, Nq, d), against its whole cache (contiguous (B, Hkv, S_cap, d) or a
+    paged pool with ``block_table``); seq_lens count the cached tokens, the Nq
+    new ones included.  ``max_seq_len`` defaults to the layout's capacity."""
+    if q.dim() != 4:
+        raise ValueError("expected q (B, Hq, Nq, d)")
+    B, Hq, Nq, d = q.shape
+    c = _cache_layout(q, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
+    if max_seq_len is None:
+        max_seq_len = c.bound
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().fa_chunked_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+                                    c.block_size, c.max_blocks, c.capacity, int(max_seq_len),
+                                    _ptr(out), _ptr(lse), B, Hq, c.Hkv, Nq, d, int(bool(causal)), float(scale),
+                                    _dtype_code(q), _stream(stream)))
+    return out, lse
+
+
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int, split_tokens: int = 0) -> int:
     return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens))
 
@@ -130,34 +213,11 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
     with ``block_table`` (B, max_blocks) int32, a paged pool
     (num_blocks, block_size, Hkv, d).  ``max_seq_len`` bounds seq_lens; it
     defaults to the capacity of the layout (no device read-back)."""
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
-        _dev(t, n)
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
     B, Hq, d = q.shape
-    paged = block_table is not None
-    if paged:
-        _dev(block_table, "block_table")
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
-            raise ValueError("block_table must be int32 (B, max_blocks)")
-        nblk, bs, Hkv, dk = k_cache.shape
-        if block_size and block_size != bs:
-            raise ValueError("block_size disagrees with the pool shape")
-        block_size = bs
-        capacity = nblk
-        max_blocks = block_table.shape[1]
-        bound = max_blocks * bs
-    else:
-        Bc, Hkv, cap, dk = k_cache.shape
-        if Bc != B:
-            raise ValueError("cache batch != q batch")
-        capacity = cap
-        max_blocks = 0
-        bound = cap
-    if dk != d or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q and caches disagree in head dim, shape or dtype")
+    c = _cache_layout(q, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
+    Hkv, paged, block_size, capacity, max_blocks = c.Hkv, c.paged, c.block_size, c.capacity, c.max_blocks
     if max_seq_len is None:
-        max_seq_len = bound
+        max_seq_len = c.bound
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens)

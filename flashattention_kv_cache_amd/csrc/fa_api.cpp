@@ -69,6 +69,27 @@ int check_decode_sizes(int B, int Hq, int Hkv, int d, int max_seq_len, int split
   return FA_OK;
 }
 
+// Shape of a KV cache as the cached-key entry points take it (contiguous or paged).
+int check_cache_layout(const int32_t* block_table, int block_size, int max_blocks_per_seq, int kv_capacity,
+                       int max_seq_len) {
+  if (max_seq_len < 0) return fail(FA_ERR_INVALID, "max_seq_len %d must be >= 0", max_seq_len);
+  if (block_table) {
+    if (!is_pow2(block_size) || block_size > 1024)
+      return fail(FA_ERR_INVALID, "block_size %d must be a power of two in [1, 1024]", block_size);
+    if (kv_capacity < 1) return fail(FA_ERR_INVALID, "paged pool must hold at least one block");
+    if (max_blocks_per_seq < 1) return fail(FA_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+    if ((long long)max_blocks_per_seq * block_size < max_seq_len)
+      return fail(FA_ERR_INVALID, "max_blocks_per_seq (%d) * block_size (%d) < max_seq_len (%d)",
+                  max_blocks_per_seq, block_size, max_seq_len);
+    if (reinterpret_cast<uintptr_t>(block_table) & 3u) return fail(FA_ERR_INVALID, "block_table must be 4-byte aligned");
+  } else {
+    if (kv_capacity < max_seq_len || kv_capacity < 1)
+      return fail(FA_ERR_INVALID, "contiguous cache capacity %d must be >= max(1, max_seq_len %d)", kv_capacity,
+                  max_seq_len);
+  }
+  return FA_OK;
+}
+
 int max_splits_for(int max_seq_len, int split_tokens) {
   return max_seq_len <= split_tokens ? 1 : (max_seq_len + split_tokens - 1) / split_tokens;
 }
@@ -77,7 +98,7 @@ int max_splits_for(int max_seq_len, int split_tokens) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
@@ -113,6 +134,80 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
   fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = dtype == FA_BF16 ? fa::launch_prefill_bf16(a, st) : fa::launch_prefill_f32(a, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fa_chunked_prefill(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+                       void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int d,
+                       int causal, float scale, int dtype, void* stream) {
+  if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1)
+    return fail(FA_ERR_INVALID, "B=%d Hq=%d Hkv=%d Nq=%d: sizes must be >= 0 and heads >= 1", B, Hq, Hkv, Nq);
+  if (Hq % Hkv) return fail(FA_ERR_INVALID, "num_kv_heads (%d) must divide num_heads (%d)", Hkv, Hq);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64 or 128)", d);
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
+  int st0 = check_cache_layout(block_table, block_size, max_blocks_per_seq, kv_capacity, max_seq_len);
+  if (st0 != FA_OK) return st0;
+  if (causal && Nq > max_seq_len)
+    return fail(FA_ERR_INVALID, "causal chunk of Nq=%d queries exceeds max_seq_len=%d", Nq, max_seq_len);
+  if (B == 0 || Nq == 0) return ok();
+  if (!q || !k_cache || !v_cache || !seq_lens || !o) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(FA_ERR_INVALID, "seq_lens must be 4-byte aligned");
+  const long long rows = (long long)B * Hq * Nq;
+  if (rows * d >= (1ll << 40)) return fail(FA_ERR_UNSUPPORTED, "problem too large");
+
+  fa::PrefillArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = 0; a.d = d;
+  a.causal = causal; a.scale = scale;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.block_size = block_table ? block_size : 0;
+  a.log2_block_size = block_table ? ilog2(block_size) : 0;
+  a.max_blocks_per_seq = block_table ? max_blocks_per_seq : 0;
+  a.kv_capacity = kv_capacity;
+  a.max_seq_len = max_seq_len;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dtype == FA_BF16 ? fa::launch_prefill_bf16(a, st) : fa::launch_prefill_f32(a, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* seq_lens, const int32_t* block_table,
+                 int block_size, int max_blocks_per_seq, int kv_capacity,
+                 int B, int Hkv, int n_new, int d, int dtype, void* stream) {
+  if (B < 0 || Hkv < 1 || n_new < 0 || d < 1)
+    return fail(FA_ERR_INVALID, "B=%d Hkv=%d n_new=%d d=%d: need B, n_new >= 0 and Hkv, d >= 1", B, Hkv, n_new, d);
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  const int es = dtype == FA_BF16 ? 2 : 4;
+  if ((d * es) % 16) return fail(FA_ERR_UNSUPPORTED, "a (token, head) row of %d bytes is not a multiple of 16", d * es);
+  int st0 = check_cache_layout(block_table, block_size, max_blocks_per_seq, kv_capacity, 0);
+  if (st0 != FA_OK) return st0;
+  if (B == 0 || n_new == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(FA_ERR_INVALID, "seq_lens must be 4-byte aligned");
+  if ((long long)B * Hkv > 65535) return fail(FA_ERR_UNSUPPORTED, "B * Hkv must be <= 65535");
+  if ((long long)n_new * (d * es / 16) > 0x7fffffffll) return fail(FA_ERR_UNSUPPORTED, "n_new too large");
+
+  fa::AppendArgs a{};
+  a.k_new = k_new; a.v_new = v_new; a.k = k_cache; a.v = v_cache;
+  a.seq_lens = seq_lens; a.block_table = block_table;
+  a.block_size = block_table ? block_size : 0;
+  a.log2_block_size = block_table ? ilog2(block_size) : 0;
+  a.max_blocks_per_seq = block_table ? max_blocks_per_seq : 0;
+  a.kv_capacity = kv_capacity;
+  a.B = B; a.Hkv = Hkv; a.n_new = n_new; a.row_chunks = d * es / 16;
+  hipError_t e = fa::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -18,6 +18,27 @@ struct PrefillArgs {
   int B, Hq, Hkv, Nq, Nk, d;
   int causal;
   float scale;
+  // Keys read from a KV cache (chunked prefill).  seq_lens == nullptr: plain
+  // prefill, Nk keys per head stored (B, Hkv, Nk, d).  Otherwise sequence b has
+  // seq_lens[b] cached keys, the Nq queries are its newest tokens, and K/V are
+  // a contiguous cache (B, Hkv, kv_capacity, d) when block_table == nullptr,
+  // else a pool (kv_capacity blocks, block_size, Hkv, d) read through
+  // block_table (B, max_blocks_per_seq).
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int block_size, log2_block_size, max_blocks_per_seq;
+  int kv_capacity, max_seq_len;
+};
+
+struct AppendArgs {
+  const void* k_new;           // (B, Hkv, n_new, d)
+  const void* v_new;
+  void* k;                     // contiguous (B, Hkv, kv_capacity, d) or pool (kv_capacity, bs, Hkv, d)
+  void* v;
+  const int32_t* seq_lens;     // (B) lengths after the append
+  const int32_t* block_table;  // nullptr: contiguous
+  int block_size, log2_block_size, max_blocks_per_seq, kv_capacity;
+  int B, Hkv, n_new, row_chunks;  // row_chunks: 16-byte chunks per (token, head) row
 };
 
 struct DecodeArgs {
@@ -41,6 +62,7 @@ struct DecodeArgs {
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Device helpers.

@@ -45,6 +45,8 @@
 //   * the row sum is accumulated in fp32 from the unrounded weights (a sum of
 //     the bf16-rounded weights would move the log-sum-exp by ~1e-3 on short
 //     rows).
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -144,7 +146,58 @@ struct TileCopy {
   }
 };
 
-template <int D>
+// The same tile copy from a paged pool (num_blocks, block_size, Hkv, D): the
+// 16 rows a wave copies are 16 consecutive tokens.  When they sit in one block
+// (block_size >= 16 and the tile is not the sequence's last) a wave needs one
+// block id and its lanes add fixed offsets to one scalar base; otherwise each
+// lane looks up the block of its own row.
+template <int D, bool IS_V>
+struct PagedCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int IPW = kBN / RPI / 4;
+  uint32_t off[IPW];  // byte offset of this lane's chunk from the wave's first token
+
+  __device__ void init(int wave, int lane, uint32_t slot_elems) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int local = i * RPI + lane / CPR;
+      const int row = wave * IPW * RPI + local;
+      const int c = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+      off[i] = (local * slot_elems + c * 8) * 2;
+    }
+  }
+  // Tokens tok0 .. tok0 + 15 of the sequence, all in physical block blk at
+  // slots slot0 .. slot0 + 15 (pool = slot 0 of block 0 at this KV head).
+  __device__ __forceinline__ void fast(const uint16_t* pool, int blk, int slot0, int bs, size_t slot_elems,
+                                       const uint16_t* dst_tile, int wave) const {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u16*)dst_tile + (uint32_t)(wave * IPW * RPI * D * 2);
+    const uint16_t* base = pool + ((size_t)blk * bs + slot0) * slot_elems;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) lds_dma_saddr(off[i], base, lds0 + i * 1024);
+  }
+  // Any block size, any position: tokens at or past Nk read token Nk - 1.
+  __device__ __forceinline__ void slow(const uint16_t* pool, const int32_t* trow, int key0, int Nk, int lbs,
+                                       int bs, size_t slot_elems, const uint16_t* dst_tile, int wave,
+                                       int lane) const {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u16*)dst_tile + (uint32_t)(wave * IPW * RPI * D * 2);
+    int blk[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {  // every lookup first: the copies below order memory
+      const int tok = min(key0 + wave * IPW * RPI + i * RPI + lane / CPR, Nk - 1);
+      blk[i] = trow[tok >> lbs];
+    }
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = wave * IPW * RPI + i * RPI + lane / CPR;
+      const int tok = min(key0 + row, Nk - 1);
+      const int c = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+      lds_dma_vaddr(pool + ((size_t)blk[i] * bs + (tok & (bs - 1))) * slot_elems + c * 8, lds0 + i * 1024);
+    }
+  }
+};
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb) {
   __shared__ Smem<D> sm;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
@@ -177,15 +230,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const int hl = lane >> 5;   // which half of the wave
   const int col = lane & 31;  // query column within the wave's 32 rows
   const int q0 = qb * kBM;
-  const int off = a.Nk - a.Nq;
+
+  // ---- the keys: Nk of them per head, or the cached length of sequence b
+  // (the queries being its newest tokens).  A length outside the contract, or
+  // a block id outside the pool, turns this workgroup's rows into NaN.
+  int Nk = a.Nk;
+  size_t head_rows = (size_t)a.Nk;
+  bool bad = false;
+  if (a.seq_lens) {
+    Nk = a.seq_lens[b];
+    head_rows = (size_t)a.kv_capacity;
+    bad = Nk < 0 || Nk > a.max_seq_len || (a.causal && Nk < a.Nq);
+    if (bad) Nk = 0;
+  }
+  const int off = Nk - a.Nq;
   const int last_row = min(a.Nq, q0 + kBM) - 1;
-  const int kend = a.causal ? min(a.Nk, last_row + off + 1) : a.Nk;
+  int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
+  if (bad) kend = 0;
+  const int32_t* trow = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
+  if (PAGED && !bad) {
+    // every token a copy may touch: the visited tiles, clamped to the sequence
+    const int ntok = min(((kend + kBN - 1) / kBN) * kBN, Nk);
+    const int ne = (ntok + a.block_size - 1) >> a.log2_block_size;
+    int oob = 0;
+    for (int i = threadIdx.x; i < ne; i += kThreads) {
+      const int e = trow[i];
+      oob |= (e < 0) | (e >= a.kv_capacity);
+    }
+    if (__syncthreads_or(oob)) {
+      bad = true;
+      kend = 0;
+    }
+  }
   const int n_tiles = (kend + kBN - 1) / kBN;
   // tiles below this index need no mask for any row of the workgroup
-  const int n_clean = a.causal ? min((q0 + off + 1) / kBN, a.Nk / kBN) : a.Nk / kBN;
+  const int n_clean = a.causal ? min((q0 + off + 1) / kBN, Nk / kBN) : Nk / kBN;
 
-  const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
-  const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (PAGED ? (size_t)g * D : (size_t)(b * a.Hkv + g) * head_rows * D);
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (PAGED ? (size_t)g * D : (size_t)(b * a.Hkv + g) * head_rows * D);
 
   // ---- Q^T operand fragments, kept in registers
   const int qrow = q0 + wave * 32 + col;
@@ -204,10 +286,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   float m = -INFINITY, l0 = 0.f, l1 = 0.f;
   const float c = a.scale * kLog2e;
 
-  TileCopy<D, false> kcp;
-  TileCopy<D, true> vcp;
-  kcp.init(wave, lane);
-  vcp.init(wave, lane);
+  using KCopy = typename std::conditional<PAGED, PagedCopy<D, false>, TileCopy<D, false>>::type;
+  using VCopy = typename std::conditional<PAGED, PagedCopy<D, true>, TileCopy<D, true>>::type;
+  KCopy kcp;
+  VCopy vcp;
+  const size_t slot_elems = (size_t)a.Hkv * D;  // paged: elements between consecutive slots
+  const int lbs = a.log2_block_size, bsz = a.block_size;
+  const bool one_block = bsz >= 16;             // paged: a wave's 16 tokens share a block
+  if constexpr (PAGED) {
+    kcp.init(wave, lane, (uint32_t)slot_elems);
+    vcp.init(wave, lane, (uint32_t)slot_elems);
+  } else {
+    kcp.init(wave, lane);
+    vcp.init(wave, lane);
+  }
+  // Block id of the first of the 16 tokens this wave copies from tile t
+  // (clamped to the sequence; loaded a stage ahead of its use).
+  auto entry = [&](int t) { return trow[min(t * kBN + wave * 16, Nk - 1) >> lbs]; };
+  int eK = 0, eV = 0;  // paged, one_block: block ids for the next stage's K and V copies
+  // Tile t of K or V (buffer dst); e = its block id when one_block.
+  auto copy_k = [&](uint16_t* dst, int t, int e) {
+    if constexpr (PAGED) {
+      const int tok0 = t * kBN + wave * 16;
+      if (one_block && tok0 + 16 <= Nk)
+        kcp.fast(kg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
+      else
+        kcp.slow(kg, trow, t * kBN, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+    } else {
+      kcp.copy(kg, dst, t * kBN, Nk, wave, lane);
+    }
+  };
+  auto copy_v = [&](uint16_t* dst, int t, int e) {
+    if constexpr (PAGED) {
+      const int tok0 = t * kBN + wave * 16;
+      if (one_block && tok0 + 16 <= Nk)
+        vcp.fast(vg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
+      else
+        vcp.slow(vg, trow, t * kBN, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+    } else {
+      vcp.copy(vg, dst, t * kBN, Nk, wave, lane);
+    }
+  };
 
   // LDS element offset of this lane's K operand (row kb*32 + col, logical
   // 16-byte chunk ks*2 + hl), and of its V^T transposed reads.
@@ -241,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // t*64 + kb*32 + 8*(r/4) + 4*hl + r%4, so one compare against a per-lane
   // limit decides each element.
   auto mask = [&](f32x16_t (&sacc)[2], int t) {
-    const int lim = (a.causal ? min(qrow + off, a.Nk - 1) : a.Nk - 1) - (t * kBN + hl * 4);
+    const int lim = (a.causal ? min(qrow + off, Nk - 1) : Nk - 1) - (t * kBN + hl * 4);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -272,8 +391,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
                    bool with_pv) {
     const int kb_next = (t + 1) & 1;  // K(t+1)
-    if (t + 2 < n_tiles) kcp.copy(kg, sm.k[t & 1], (t + 2) * kBN, a.Nk, wave, lane);
-    vcp.copy(vg, sm.v[t & 1], t * kBN, a.Nk, wave, lane);
+    if (t + 2 < n_tiles) copy_k(sm.k[t & 1], t + 2, eK);
+    copy_v(sm.v[t & 1], t, eV);
+    if (PAGED && one_block) {
+      eK = entry(t + 3);
+      eV = entry(t + 1);
+      asm volatile("" ::: "memory");  // the lookups fly during this stage
+    }
 
     // A rescale decided in the previous stage applies to O once PV(t-2) (its
     // weights used the old reference) is in, i.e. now, before PV(t-1) starts.
@@ -357,8 +481,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // unconditional so that, on every path into the loop, the Q fragments are
   // known to have arrived (otherwise each QK^T MFMA waits on vmcnt).
   if (n_tiles > 0) {
-    kcp.copy(kg, sm.k[0], 0, a.Nk, wave, lane);
-    if (n_tiles > 1) kcp.copy(kg, sm.k[1], kBN, a.Nk, wave, lane);
+    const bool look = PAGED && one_block;
+    copy_k(sm.k[0], 0, look ? entry(0) : 0);
+    if (n_tiles > 1) copy_k(sm.k[1], 1, look ? entry(1) : 0);
+    if (look) {
+      eK = entry(2);
+      eV = entry(0);
+    }
   }
   wait_all_vmem();
   __syncthreads();
@@ -387,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- epilogue: one division, bf16 output, natural-log LSE
   const float lt = halves_sum(l0 + l1);
   if (qrow >= a.Nq) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
   uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qrow) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -400,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       *reinterpret_cast<u32x2_t*>(op + d) = w;
     }
   if (a.lse && hl == 0)
-    a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+    a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -409,10 +538,14 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.Nq + kBM - 1) / kBM;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.d == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+  const bool paged = a.block_table != nullptr;
+  if (a.d == 64) {
+    if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+  } else {
+    if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+  }
   return hipGetLastError();
 }
 

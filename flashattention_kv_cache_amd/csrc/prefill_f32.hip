@@ -21,7 +21,7 @@ constexpr int kRows = 64;   // query rows per workgroup (one per lane)
 constexpr int kKeys = 32;   // keys per LDS tile
 constexpr int kSub = 8;     // keys per softmax update
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   __shared__ float4 Ks[kKeys * D / 4];
   __shared__ float4 Vs[kKeys * D / 4];
@@ -36,16 +36,53 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 
   const int row = qb * kRows + lane;
   const bool row_ok = row < a.Nq;
-  const int off = a.Nk - a.Nq;
+
+  // Keys: Nk per head, or the cached length of sequence b (its newest Nq
+  // tokens being the queries).  A length outside the contract or a block id
+  // outside the pool turns the rows into NaN.
+  int Nk = a.Nk;
+  size_t head_rows = (size_t)a.Nk;
+  bool bad = false;
+  if (a.seq_lens) {
+    Nk = a.seq_lens[b];
+    head_rows = (size_t)a.kv_capacity;
+    bad = Nk < 0 || Nk > a.max_seq_len || (a.causal && Nk < a.Nq);
+    if (bad) Nk = 0;
+  }
+  const int off = Nk - a.Nq;
   // keys [0, lim) are visible to this row
-  const int lim = a.causal ? min(a.Nk, row + off + 1) : a.Nk;
+  const int lim = a.causal ? min(Nk, row + off + 1) : Nk;
   const int last_row = min(a.Nq, (qb + 1) * kRows) - 1;
-  const int kend = a.causal ? min(a.Nk, last_row + off + 1) : a.Nk;
+  int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
+  if (bad) kend = 0;
+  const int32_t* trow = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
+  if (PAGED && kend > 0) {
+    const int ntok = min(((kend + kKeys - 1) / kKeys) * kKeys, Nk);  // rows the staging loop reads
+    const int ne = (ntok + a.block_size - 1) >> a.log2_block_size;
+    int oob = 0;
+    for (int i = lane; i < ne; i += 64) {
+      const int e = trow[i];
+      oob |= (e < 0) | (e >= a.kv_capacity);
+    }
+    if (__syncthreads_or(oob)) {
+      bad = true;
+      kend = 0;
+    }
+  }
 
   const float c = a.scale * kLog2e;  // scores kept in log2 units
   const float* qp = reinterpret_cast<const float*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq + min(row, a.Nq - 1)) * D;
-  const float* kp = reinterpret_cast<const float*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
-  const float* vp = reinterpret_cast<const float*>(a.v) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  // first element of key/value row j of this head
+  auto kv_row = [&](const void* base, int j) -> const float4* {
+    const float* p = reinterpret_cast<const float*>(base);
+    if constexpr (PAGED) {
+      const int e = trow[j >> a.log2_block_size];
+      return reinterpret_cast<const float4*>(
+          p + (((size_t)e * a.block_size + (j & (a.block_size - 1))) * a.Hkv + g) * D);
+    } else {
+      return reinterpret_cast<const float4*>(p + ((size_t)(b * a.Hkv + g) * head_rows + j) * D);
+    }
+  };
 
   float qr[D];
 #pragma unroll
@@ -63,9 +100,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     for (int i = lane; i < kKeys * D / 4; i += 64) {
       const int r = i / (D / 4), cc = i % (D / 4);
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (k0 + r < a.Nk) {
-        kv = reinterpret_cast<const float4*>(kp + (size_t)(k0 + r) * D)[cc];
-        vv = reinterpret_cast<const float4*>(vp + (size_t)(k0 + r) * D)[cc];
+      if (k0 + r < Nk) {
+        kv = kv_row(a.k, k0 + r)[cc];
+        vv = kv_row(a.v, k0 + r)[cc];
       }
       Ks[i] = kv;
       Vs[i] = vv;
@@ -117,12 +154,13 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   }
 
   if (!row_ok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = bad ? __builtin_nanf("") : l > 0.f ? 1.f / l : 0.f;
   float* op = reinterpret_cast<float*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + row) * D;
 #pragma unroll
   for (int e = 0; e < D; e += 4)
     *reinterpret_cast<float4*>(op + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
-  if (a.lse) a.lse[(size_t)(b * a.Hq + h) * a.Nq + row] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+  if (a.lse)
+    a.lse[(size_t)(b * a.Hq + h) * a.Nq + row] = bad ? __builtin_nanf("") : l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -131,10 +169,14 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.Nq + kRows - 1) / kRows;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.d == 64)
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)grid), dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)grid), dim3(64), 0, s, a);
+  const bool paged = a.block_table != nullptr;
+  if (a.d == 64) {
+    if (paged) hipLaunchKernelGGL((prefill_f32_kernel<64, true>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((prefill_f32_kernel<64, false>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  } else {
+    if (paged) hipLaunchKernelGGL((prefill_f32_kernel<128, true>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((prefill_f32_kernel<128, false>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -304,3 +304,47 @@ C3 = DecodeWorkload("contiguous decode bf16, B=64 Hq=32 Hkv=8 d=128 L~U[1024,819
 C4 = PrefillWorkload("long-context causal GQA prefill bf16, Hq=64 Hkv=8 N=32768 d=128", 1, 64, 8, 32768, 32768, 128, True, "bf16", 1003)
 C5 = DecodeWorkload("paged decode bf16, B=128 Hq=32 Hkv=8 d=128 bs=16 L~U[512,32768]", 128, 32, 8, 128, 512, 32768, True, "bf16", 1004)
 WORKLOADS = (C1, C2, C3, C4, C5)
+
+
+@dataclass(frozen=True)
+class ChunkedWorkload:
+    """n_new-token chunks appended to paged caches, then attended causally
+    against each whole sequence."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    chunk: int
+    past_lo: int
+    past_hi: int
+    block_size: int
+    dtype: str
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self, seq_lens) -> int:
+        """2 flop per multiply-add over the unmasked (query, key) pairs of every
+        sequence: query i of a sequence of L keys sees L - chunk + i + 1 keys."""
+        n = self.chunk
+        pairs = sum(n * (int(L) - n) + n * (n + 1) // 2 for L in seq_lens)
+        return 4 * self.d * self.Hq * pairs
+
+    def append_bytes(self) -> int:
+        """The append reads and writes every new K and V element once."""
+        es = 4 if self.dtype == "f32" else 2
+        return 2 * 2 * self.B * self.Hkv * self.chunk * self.d * es
+
+
+def chunked_inputs(w: ChunkedWorkload) -> ChunkedInputs:
+    return make_chunked_inputs(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.seed, chunk=w.chunk,
+                               past_range=(w.past_lo, w.past_hi), paged=True, block_size=w.block_size)
+
+
+# A prompt chunk of 1024 tokens per sequence against paged caches that already
+# hold 1024..7168 tokens (the prefill half of a chunked-prefill serving step).
+CHUNKED = ChunkedWorkload("chunked prefill bf16 vs paged cache, B=4 Hq=32 Hkv=8 d=128 chunk=1024 "
+                          "past~U[1024,7168] bs=16", 4, 32, 8, 128, 1024, 1024, 7168, 16, "bf16", 1005)

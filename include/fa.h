@@ -154,6 +154,78 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
               int B, int Hq, int Hkv, int d, float scale, int dtype,
               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_kv_append — write the keys and values of n_new new tokens per sequence
+ * into a KV cache, at positions L_b - n_new .. L_b - 1 of sequence b (L_b =
+ * seq_lens[b], the length AFTER the append).  A pure copy: the cache receives
+ * the given bits unchanged.
+ *
+ * Defined by: "Module 09: Efficient Attention", section "Code: A Paged KV Cache
+ * from Scratch" (appending token t writes slot t % block_size of physical block
+ * block_table[t / block_size]); "Генерация и KV-кэш", section "KV-кэш для
+ * одной головы на NumPy" (each generated token's k and v are appended to the
+ * cache before attention reads it).  Claiming blocks is the caller's job: the
+ * table must already list the block of every written position.
+ *
+ *   k_new, v_new (B, Hkv, n_new, d)   input dtype (the layout fa_prefill takes k, v in)
+ *   k_cache,     contiguous: (B, Hkv, kv_capacity, d)
+ *   v_cache      paged:      (kv_capacity, block_size, Hkv, d) shared pool
+ *   seq_lens     (B) int32, device
+ *   block_table  NULL (contiguous) or (B, max_blocks_per_seq) int32, device
+ *
+ * Contract: B, n_new >= 0; Hkv >= 1; d * element size a multiple of 16 bytes;
+ * n_new <= L_b <= capacity (contiguous: kv_capacity; paged:
+ * max_blocks_per_seq * block_size); block ids read lie in [0, kv_capacity).
+ * The new rows must not overlap the cache.  Device-side violations are
+ * skipped: a sequence with an L_b outside the contract, or a token whose block
+ * id is out of range, is not written, and nothing outside the cache is ever
+ * written.  Positions other than the n_new new ones are left untouched.
+ */
+int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* seq_lens, const int32_t* block_table,
+                 int block_size, int max_blocks_per_seq, int kv_capacity,
+                 int B, int Hkv, int n_new, int d, int dtype, void* stream);
+
+/*
+ * fa_chunked_prefill — attention of the Nq newest tokens of each sequence
+ * against that sequence's whole KV cache (its own new keys included, appended
+ * beforehand, e.g. by fa_kv_append): the prefill of one chunk of a long prompt,
+ * or of a prompt that extends a cached prefix.  Query i of sequence b is the
+ * token at position L_b - Nq + i and, when causal, sees keys
+ * j <= L_b - Nq + i: the causal mask aligned to the bottom-right corner
+ * ("Генерация и KV-кэш", section "Три ловушки", item 2).  Nq = 1 is a decode
+ * step (fa_decode computes the same thing with a split-K launch).
+ *
+ * Defined by: the same passages as fa_prefill (tiled exact attention with the
+ * streaming softmax) with keys read through the cache layout of fa_decode
+ * ("Module 09: Efficient Attention", section "Code: A Paged KV Cache from
+ * Scratch").
+ *
+ *   q            (B, Hq, Nq, d)          input dtype
+ *   k_cache,     contiguous: (B, Hkv, kv_capacity, d)
+ *   v_cache      paged:      (kv_capacity, block_size, Hkv, d) shared pool
+ *   seq_lens     (B) int32, device: cached length L_b, the Nq new tokens included
+ *   block_table  NULL (contiguous) or (B, max_blocks_per_seq) int32, device
+ *   max_seq_len  host-side upper bound on every L_b
+ *   o            (B, Hq, Nq, d) output, input dtype
+ *   lse          (B, Hq, Nq) fp32 output or NULL (as for fa_prefill)
+ *   causal       1 for a prompt chunk; 0 lets every query see all L_b keys
+ *
+ * Contract: as fa_prefill for B, heads, d, scale; 0 <= L_b <= max_seq_len and,
+ * when causal, L_b >= Nq; contiguous kv_capacity >= max_seq_len; paged:
+ * block_size a power of two in [1, 1024], max_blocks_per_seq * block_size >=
+ * max_seq_len and every block id read in [0, kv_capacity).  Device-side
+ * violations (an L_b outside that range, an out-of-range block id) are
+ * detected by the kernel: the affected rows of o and lse come out NaN and no
+ * out-of-range address is read.
+ */
+int fa_chunked_prefill(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+                       void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int d,
+                       int causal, float scale, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

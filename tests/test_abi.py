@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string",
-                 "fa_last_error", "fa_abi_version", "fa_decode_split_tokens"):
+                 "fa_last_error", "fa_abi_version", "fa_decode_split_tokens", "fa_kv_append",
+                 "fa_chunked_prefill"):
         assert want in names
 
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol(fa):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(fa.SIGNATURES) == set(declared_functions())
-    assert L.fa_abi_version() == 1
+    assert L.fa_abi_version() == 2
 
 
 def test_status_strings(fa):
@@ -137,6 +138,80 @@ def test_decode_empty_batch_is_a_noop(fa):
     assert decode(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, B=0) == FA_OK
 
 
+def chunked(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, o=A, lse=A,
+            B=2, Hq=8, Hkv=2, Nq=16, d=128, causal=1, scale=0.1, dtype=BF16):
+    P = ctypes.c_void_p
+    return fa.lib().fa_chunked_prefill(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, P(o), P(lse),
+                                       B, Hq, Hkv, Nq, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), FA_ERR_INVALID, "divide"),
+    (dict(Nq=-1), FA_ERR_INVALID, ">= 0"),
+    (dict(d=96), FA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=9), FA_ERR_INVALID, "dtype"),
+    (dict(causal=3), FA_ERR_INVALID, "causal"),
+    (dict(scale=0.0), FA_ERR_INVALID, "scale"),
+    (dict(maxlen=-1), FA_ERR_INVALID, "max_seq_len"),
+    (dict(Nq=65, maxlen=64), FA_ERR_INVALID, "exceeds max_seq_len"),
+    (dict(cap=32, maxlen=64), FA_ERR_INVALID, "capacity"),
+    (dict(table=A, bs=24), FA_ERR_INVALID, "power of two"),
+    (dict(table=A, bs=16, mbps=3), FA_ERR_INVALID, "max_blocks_per_seq"),
+    (dict(table=A, cap=0), FA_ERR_INVALID, "at least one block"),
+    (dict(table=A + 2), FA_ERR_INVALID, "4-byte"),
+    (dict(lens=A + 2), FA_ERR_INVALID, "4-byte"),
+    (dict(q=0), FA_ERR_INVALID, "null"),
+    (dict(lens=0), FA_ERR_INVALID, "null"),
+    (dict(o=MIS), FA_ERR_INVALID, "aligned"),
+])
+def test_chunked_prefill_rejects(fa, kw, status, msg):
+    assert chunked(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_chunked_prefill_empty_is_a_noop(fa):
+    assert chunked(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, B=0) == FA_OK
+    assert chunked(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, Nq=0) == FA_OK
+    # a non-causal chunk may be longer than any cached sequence
+    assert chunked(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, Nq=0, causal=0, maxlen=8) == FA_OK
+
+
+def append(fa, kn=A, vn=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, B=2, Hkv=2, n=4, d=128,
+           dtype=BF16):
+    P = ctypes.c_void_p
+    return fa.lib().fa_kv_append(P(kn), P(vn), P(k), P(v), P(lens), P(table), bs, mbps, cap, B, Hkv, n, d,
+                                 dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(B=-1), FA_ERR_INVALID, "B=-1"),
+    (dict(Hkv=0), FA_ERR_INVALID, "Hkv"),
+    (dict(n=-2), FA_ERR_INVALID, "n_new"),
+    (dict(dtype=4), FA_ERR_INVALID, "dtype"),
+    (dict(d=12), FA_ERR_UNSUPPORTED, "multiple of 16"),
+    (dict(d=6, dtype=F32), FA_ERR_UNSUPPORTED, "multiple of 16"),
+    (dict(cap=0), FA_ERR_INVALID, "capacity"),
+    (dict(table=A, bs=3), FA_ERR_INVALID, "power of two"),
+    (dict(table=A, mbps=0), FA_ERR_INVALID, "max_blocks_per_seq"),
+    (dict(table=A, cap=0), FA_ERR_INVALID, "at least one block"),
+    (dict(kn=0), FA_ERR_INVALID, "null"),
+    (dict(lens=0), FA_ERR_INVALID, "null"),
+    (dict(v=MIS), FA_ERR_INVALID, "aligned"),
+    (dict(lens=A + 1), FA_ERR_INVALID, "4-byte"),
+    (dict(B=40000, Hkv=2), FA_ERR_UNSUPPORTED, "65535"),
+])
+def test_kv_append_rejects(fa, kw, status, msg):
+    assert append(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_kv_append_empty_is_a_noop(fa):
+    assert append(fa, kn=0, vn=0, k=0, v=0, lens=0, B=0) == FA_OK
+    assert append(fa, kn=0, vn=0, k=0, v=0, lens=0, n=0) == FA_OK
+    # d = 8 fp32 is 32 bytes a row: accepted (any d whose row is whole 16-byte chunks)
+    assert append(fa, kn=0, vn=0, k=0, v=0, lens=0, n=0, d=8, dtype=F32) == FA_OK
+
+
 def test_no_cpu_fallback_without_gpu(fa):
     """On a machine without a GPU the binding raises instead of computing."""
     import torch
@@ -145,3 +220,8 @@ def test_no_cpu_fallback_without_gpu(fa):
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         fa.prefill(q, q, q)
+    lens = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.chunked_prefill(q, q, q, lens)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.kv_append(q, q, q, q, lens)

@@ -1,0 +1,244 @@
+"""KV append and chunked prefill through the C ABI, against the fp64 oracle.
+
+The append is a copy: the cache after the GPU append must equal, bit for bit
+(NaN poison included), the cache after the oracle's append.  Chunked prefill
+uses the tolerances of every other attention output (fp32 max-abs 1e-5; bf16
+max-abs 2e-2 and mean-abs 2e-3; LSE 1e-4).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max=1e-5, mean=1e-5), "bf16": dict(max=2e-2, mean=2e-3)}
+LSE_TOL = 1e-4
+DEV = "cuda"
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def check(o_gpu, lse_gpu, O_ref, lse_ref, dt, what=""):
+    O = o_gpu.detach().to("cpu", torch.float64).numpy()
+    assert O.shape == np.asarray(O_ref).shape
+    assert np.isfinite(O).all(), f"{what}: non-finite output"
+    err = np.abs(O - O_ref)
+    assert err.max() <= TOL[dt]["max"], f"{what}: max abs err {err.max():.3e}"
+    assert err.mean() <= TOL[dt]["mean"], f"{what}: mean abs err {err.mean():.3e}"
+    L = lse_gpu.detach().to("cpu", torch.float64).numpy()
+    e = np.abs(L - lse_ref).max()
+    assert e <= LSE_TOL, f"{what}: LSE err {e:.3e}"
+
+
+def gpu_append(fa, ci):
+    """Copy the cache to the GPU and append the chunk there."""
+    kc, vc = ci.k_cache.to(DEV), ci.v_cache.to(DEV)
+    lens = ci.seq_lens.to(DEV)
+    table = ci.block_table.to(DEV) if ci.paged else None
+    fa.kv_append(ci.k_new.to(DEV), ci.v_new.to(DEV), kc, vc, lens, block_table=table)
+    return kc, vc, lens, table
+
+
+def oracle_append(ci):
+    if ci.paged:
+        return oracle.append_batch(ci.k_cache, ci.v_cache, ci.block_table, ci.seq_lens, ci.k_new, ci.v_new,
+                                   ci.block_size)
+    return oracle.append_batch_contiguous(ci.k_cache, ci.v_cache, ci.seq_lens, ci.k_new, ci.v_new)
+
+
+# ----------------------------------------------------------------------------
+# append: bit-exact
+# ----------------------------------------------------------------------------
+APPEND_CASES = [
+    # B, Hkv, d, chunk, past_lens, paged, block_size
+    (3, 2, 128, 9, [0, 23, 16], True, 16),
+    (3, 2, 64, 1, [0, 23, 16], True, 4),
+    (2, 8, 128, 130, [5, 1000], True, 1),
+    (2, 8, 128, 300, [64, 7], True, 128),
+    (3, 1, 64, 17, [0, 40, 3], False, 0),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("case", APPEND_CASES, ids=lambda c: "B{}_Hkv{}_d{}_n{}_{}_bs{}".format(
+    c[0], c[1], c[2], c[3], "paged" if c[5] else "contig", c[6]))
+def test_kv_append_is_bit_exact(fa, case, dt):
+    B, Hkv, d, n, past, paged, bs = case
+    note(f"append {dt} {case}")
+    ci = W.make_chunked_inputs(B, 2 * Hkv, Hkv, d, dt, seed=77 + n, chunk=n, past_lens=past, paged=paged,
+                               block_size=max(bs, 1), spare_blocks=2 if paged else 0)
+    kc, vc, _, _ = gpu_append(fa, ci)
+    torch.cuda.synchronize()
+    kr, vr = oracle_append(ci)
+    assert torch.equal(bits(kc), bits(kr)) and torch.equal(bits(vc), bits(vr))
+
+
+def test_kv_append_skips_invalid_sequences(fa):
+    """A sequence whose length breaks the contract, or whose block id is out of
+    range, is left unwritten; the others are written."""
+    ci = W.make_chunked_inputs(3, 2, 1, 64, "bf16", 5, chunk=4, past_lens=[10, 10, 10], block_size=4)
+    lens = ci.seq_lens.clone()
+    lens[0] = 2                                   # shorter than the chunk
+    table = ci.block_table.clone()
+    table[1, 3] = 10_000                          # the block of positions 12..13 is out of range
+    kc, vc = ci.k_cache.to(DEV), ci.v_cache.to(DEV)
+    fa.kv_append(ci.k_new.to(DEV), ci.v_new.to(DEV), kc, vc, lens.to(DEV), block_table=table.to(DEV))
+    torch.cuda.synchronize()
+    good = W.ChunkedInputs(ci.q[2:], ci.k_new[2:], ci.v_new[2:], ci.k_cache, ci.v_cache, ci.seq_lens[2:],
+                           ci.block_table[2:], 4, ci.kv_capacity, ci.max_seq_len)
+    kr, _ = oracle_append(good)
+    # sequence 1: positions 10, 11 (block table[1, 2]) are written, 12, 13 are not
+    kr[int(ci.block_table[1, 2]), 2:4] = ci.k_new[1, :, 0:2].transpose(0, 1)
+    assert torch.equal(bits(kc), bits(kr))
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill: small shapes, every element
+# ----------------------------------------------------------------------------
+CHUNK_CASES = [
+    # B, Hq, Hkv, d, chunk, past_lens, paged, block_size, causal, shared_prefix_blocks
+    (2, 4, 2, 128, 70, [130, 0], True, 16, True, 0),
+    (2, 4, 2, 64, 128, [64, 200], True, 16, True, 0),
+    (1, 8, 2, 128, 200, [333], True, 32, True, 0),
+    (2, 4, 1, 128, 65, [7, 100], True, 4, True, 0),        # block smaller than a wave's 16 rows
+    (1, 4, 2, 64, 33, [90], True, 1, True, 0),
+    (2, 4, 4, 128, 64, [256, 3], True, 128, True, 0),
+    (3, 4, 2, 128, 50, [80, 96, 150], True, 16, True, 4),  # a shared 64-token prefix
+    (2, 4, 2, 128, 70, [130, 0], False, 0, True, 0),       # contiguous cache
+    (2, 8, 4, 64, 100, [20, 300], False, 0, True, 0),
+    (2, 4, 2, 128, 40, [100, 10], True, 16, False, 0),     # every query sees the whole cache
+]
+
+
+def _chunk_ids(c):
+    return "B{}_Hq{}_Hkv{}_d{}_n{}_{}_bs{}_{}{}".format(c[0], c[1], c[2], c[3], c[4], "paged" if c[6] else "contig",
+                                                       c[7], "causal" if c[8] else "full", f"_share{c[9]}" if c[9] else "")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=_chunk_ids)
+def test_chunked_prefill_small(fa, case, dt):
+    B, Hq, Hkv, d, n, past, paged, bs, causal, share = case
+    note(f"chunked prefill {dt} {case}")
+    ci = W.make_chunked_inputs(B, Hq, Hkv, d, dt, seed=300 + n + d, chunk=n, past_lens=past, paged=paged,
+                               block_size=max(bs, 1), s_cap=(max(past) + n + 37) if not paged else None,
+                               spare_blocks=3 if paged else 0, shared_prefix_blocks=share)
+    kc, vc, lens, table = gpu_append(fa, ci)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.chunked_prefill(ci.q.to(DEV), kc, vc, lens, block_table=table, max_seq_len=ci.max_seq_len,
+                                causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    kr, vr = oracle_append(ci)
+    O_ref, lse_ref = oracle.chunked_prefill(ci.q, kr, vr, ci.seq_lens, scale, causal,
+                                            ci.block_table, ci.block_size)
+    check(o, lse, O_ref, lse_ref, dt, f"chunked {case}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunked_prefill_without_past_is_prefill_bit_for_bit(fa, dt, d):
+    """A first chunk (empty past) through a paged or contiguous cache takes the
+    same arithmetic, in the same order, as fa_prefill on the gathered keys."""
+    n = 300
+    for paged in (True, False):
+        ci = W.make_chunked_inputs(1, 8, 2, d, dt, seed=41 + d, chunk=n, past_lens=[0], paged=paged,
+                                   block_size=16)
+        kc, vc, lens, table = gpu_append(fa, ci)
+        o, lse = fa.chunked_prefill(ci.q.to(DEV), kc, vc, lens, block_table=table, max_seq_len=n)
+        o2, lse2 = fa.prefill(ci.q.to(DEV), ci.k_new.to(DEV), ci.v_new.to(DEV), causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(o), bits(o2)) and torch.equal(bits(lse), bits(lse2)), f"paged={paged}"
+
+
+def test_chunk_of_one_token_matches_decode(fa):
+    ci = W.make_chunked_inputs(4, 8, 2, 128, "bf16", 42, chunk=1, past_lens=[0, 17, 300, 1000], block_size=16)
+    kc, vc, lens, table = gpu_append(fa, ci)
+    o, lse = fa.chunked_prefill(ci.q.to(DEV), kc, vc, lens, block_table=table, max_seq_len=ci.max_seq_len)
+    od, lsed = fa.decode(ci.q[:, :, 0].contiguous().to(DEV), kc, vc, lens, block_table=table,
+                         max_seq_len=ci.max_seq_len, split_tokens=256)
+    torch.cuda.synchronize()
+    kr, vr = oracle_append(ci)
+    O_ref, lse_ref = oracle.chunked_prefill(ci.q, kr, vr, ci.seq_lens, 1 / math.sqrt(128), True,
+                                            ci.block_table, 16)
+    check(o, lse, O_ref, lse_ref, "bf16", "chunk of 1")
+    check(od[:, :, None], lsed[:, :, None], O_ref, lse_ref, "bf16", "decode")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_chunked_prefill_flags_invalid_device_inputs_with_nan(fa, dt):
+    ci = W.make_chunked_inputs(4, 4, 2, 64, dt, 43, chunk=40, past_lens=[30, 30, 30, 30], block_size=16)
+    kc, vc, lens, table = gpu_append(fa, ci)
+    bad_lens = lens.clone()
+    bad_lens[0] = 20                       # fewer keys than the causal chunk has queries
+    bad_lens[1] = ci.max_seq_len + 1       # beyond the declared bound
+    bad_table = table.clone()
+    bad_table[2, 1] = ci.kv_capacity       # a block id outside the pool
+    o, lse = fa.chunked_prefill(ci.q.to(DEV), kc, vc, bad_lens, block_table=bad_table,
+                                max_seq_len=ci.max_seq_len)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu(), lse.cpu()
+    for b in range(3):
+        assert torch.isnan(o[b]).all() and torch.isnan(lse[b]).all(), b
+    kr, vr = oracle_append(ci)
+    O_ref, lse_ref = oracle.chunked_prefill(ci.q[3:], kr, vr, ci.seq_lens[3:], 1 / 8, True,
+                                            ci.block_table[3:], 16)
+    check(o[3:], lse[3:], O_ref, lse_ref, dt, "valid sequence next to invalid ones")
+
+
+def test_chunked_prefill_writes_nothing_outside_its_output(fa):
+    ci = W.make_chunked_inputs(2, 4, 2, 128, "bf16", 44, chunk=70, past_lens=[100, 5], block_size=16)
+    kc, vc, lens, table = gpu_append(fa, ci)
+    guard = 4096
+    buf = torch.full((2 * guard + ci.q.numel(),), 7.0, dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((2 * guard + 2 * 4 * 70,), 7.0, dtype=torch.float32, device=DEV)
+    o = buf[guard:guard + ci.q.numel()].view(ci.q.shape)
+    lse = lbuf[guard:guard + 2 * 4 * 70].view(2, 4, 70)
+    fa.chunked_prefill(ci.q.to(DEV), kc, vc, lens, block_table=table, out=o, lse=lse, max_seq_len=ci.max_seq_len)
+    torch.cuda.synchronize()
+    assert (buf[:guard] == 7).all() and (buf[-guard:] == 7).all()
+    assert (lbuf[:guard] == 7).all() and (lbuf[-guard:] == 7).all()
+
+
+# ----------------------------------------------------------------------------
+# the full-size chunked workload, in the launch configuration the benchmark times
+# ----------------------------------------------------------------------------
+def test_chunked_workload_full_size(fa):
+    w = W.CHUNKED
+    note(f"chunked workload {w.name}")
+    ci = W.chunked_inputs(w)
+    kc, vc, lens, table = gpu_append(fa, ci)
+    o, lse = fa.chunked_prefill(ci.q.to(DEV), kc, vc, lens, block_table=table, max_seq_len=ci.max_seq_len,
+                                scale=w.scale)
+    torch.cuda.synchronize()
+    # the append: the whole pool, bit for bit
+    kr, vr = oracle_append(ci)
+    assert torch.equal(bits(kc), bits(kr)) and torch.equal(bits(vc), bits(vr))
+    # sampled rows: first and last query of every sequence, the 64/128-row tile
+    # edges, and random ones
+    rng = np.random.default_rng(7)
+    rows = []
+    for b in range(w.B):
+        for i in (0, 63, 64, 127, 128, w.chunk - 1):
+            rows.append((b, int(rng.integers(w.Hq)), i))
+    rows += [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.chunk))) for _ in range(24)]
+    O_ref, lse_ref = oracle.chunked_prefill(ci.q, kr, vr, ci.seq_lens, w.scale, True, ci.block_table,
+                                            w.block_size, rows=rows)
+    idx = tuple(torch.tensor(c) for c in zip(*rows))
+    check(o.cpu()[idx], lse.cpu()[idx], O_ref, lse_ref, "bf16", "chunked workload rows")
+    # properties that hold everywhere: finite, LSE no smaller than the
+    # largest visible score would allow for one key (checked as finite here)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
