@@ -8,8 +8,8 @@ the seeded generators, which hold no attention arithmetic.
 
 Modules:
   attention  the plain definition: materialise the scores, two-pass softmax,
-             GQA head mapping, bottom-right causal mask, contiguous and paged
-             KV-cache reads (prefill and decode).
+             GQA head mapping, bottom-right causal mask and sliding window,
+             contiguous and paged KV-cache reads (prefill and decode).
   online     the pages' streaming recurrence (running max and sum, rescaling of
              earlier partials) and the merge of two partial states; used to pin
              the definition, never to produce expected values for kernels.
@@ -22,7 +22,7 @@ Every function cites the passage it follows by page title and section.  All
 functions are pinned by tests that check them against values the pages print,
 closed forms, special cases and brute force (no function is "parity unpinned").
 """
-from .attention import (kv_head_of, causal_key_limit, attention_rows, prefill,
+from .attention import (kv_head_of, causal_key_limit, window_key_start, attention_rows, prefill,
                         prefill_rows, paged_gather, decode_contiguous, decode_paged)
 from .online import online_softmax_stats, online_attention_row, merge_partials
 from .kv_bytes import kv_cache_bytes, kv_bytes_per_token
@@ -30,7 +30,7 @@ from .paged import (BlockAllocator, PagedSequence, append_token, share_prefix, a
                     append_batch_contiguous, chunked_prefill)
 
 __all__ = [
-    "kv_head_of", "causal_key_limit", "attention_rows", "prefill", "prefill_rows",
+    "kv_head_of", "causal_key_limit", "window_key_start", "attention_rows", "prefill", "prefill_rows",
     "paged_gather", "decode_contiguous", "decode_paged",
     "online_softmax_stats", "online_attention_row", "merge_partials",
     "kv_cache_bytes", "kv_bytes_per_token",

@@ -19,6 +19,12 @@ What is computed, and where the pages say so:
 * Decode: one new query against every cached key, itself included, with no
   mask ("Генерация и KV-кэш", NumPy decode step).  The cache already holds the
   new token; ``seq_lens`` counts it.
+* Sliding window: with a window of W keys, a (causal) query sees only the W
+  most recent keys, itself included ("Module 09: Efficient Attention",
+  section "Attention Mask Gallery": the printed window-3 mask over six
+  positions, where row i attends keys i-2 .. i).  Aligned like the causal
+  mask: query i sees keys j with i + (N_k - N_q) - W < j <= i + (N_k - N_q).
+  W = 0 means no window.
 * Paged read: token t of a sequence lives at
   pool[block_table[t // block_size], t % block_size] ("Module 09", "Code: A
   Paged KV Cache from Scratch").
@@ -67,12 +73,21 @@ def causal_key_limit(i: int, Nq: int, Nk: int) -> int:
     return min(Nk, max(0, i + (Nk - Nq) + 1))
 
 
-def attention_rows(q_rows, K, V, scale: float, key_limits=None):
+def window_key_start(i: int, Nq: int, Nk: int, window: int) -> int:
+    """First key visible to query row i under a sliding window of ``window``
+    keys aligned to the bottom-right corner (0 when window == 0)."""
+    if window <= 0:
+        return 0
+    return max(0, i + (Nk - Nq) - window + 1)
+
+
+def attention_rows(q_rows, K, V, scale: float, key_limits=None, key_starts=None):
     """Attention of R query rows against one head's keys.
 
-    q_rows (R, d), K and V (Nk, d); ``key_limits[r]`` keys (a prefix) are
-    visible to row r, all of them if None.  Returns O (R, d) and LSE (R,) in
-    fp64.  A row with no visible key gets O = 0 and LSE = -inf.
+    q_rows (R, d), K and V (Nk, d); keys ``key_starts[r] <= j < key_limits[r]``
+    are visible to row r (a prefix when key_starts is None, all keys when both
+    are None).  Returns O (R, d) and LSE (R,) in fp64.  A row with no visible
+    key gets O = 0 and LSE = -inf.
     """
     q_rows, K, V = _f64(q_rows), _f64(K), _f64(V)
     R, Nk = q_rows.shape[0], K.shape[0]
@@ -80,6 +95,9 @@ def attention_rows(q_rows, K, V, scale: float, key_limits=None):
     if key_limits is not None:
         lim = np.asarray(key_limits, dtype=np.int64).reshape(R, 1)
         S = np.where(np.arange(Nk)[None, :] < lim, S, -np.inf)
+    if key_starts is not None:
+        lo = np.asarray(key_starts, dtype=np.int64).reshape(R, 1)
+        S = np.where(np.arange(Nk)[None, :] >= lo, S, -np.inf)
     O = np.zeros((R, V.shape[1]))
     lse = np.full(R, -np.inf)
     live = np.isfinite(S).any(axis=1)
@@ -93,8 +111,9 @@ def attention_rows(q_rows, K, V, scale: float, key_limits=None):
     return O, lse
 
 
-def prefill(q, k, v, scale: float, causal: bool, row_block: int = 1024):
-    """Full prefill: q (B, Hq, Nq, d), k and v (B, Hkv, Nk, d).
+def prefill(q, k, v, scale: float, causal: bool, row_block: int = 1024, window: int = 0):
+    """Full prefill: q (B, Hq, Nq, d), k and v (B, Hkv, Nk, d); ``window`` > 0
+    adds the sliding-window lower bound to the causal mask.
 
     Returns O (B, Hq, Nq, d) and LSE (B, Hq, Nq), fp64.
     """
@@ -109,13 +128,14 @@ def prefill(q, k, v, scale: float, causal: bool, row_block: int = 1024):
             for r0 in range(0, Nq, row_block):
                 rows = range(r0, min(Nq, r0 + row_block))
                 lim = [causal_key_limit(i, Nq, Nk) for i in rows] if causal else None
-                o, l = attention_rows(q[b, h, r0:r0 + len(rows)], k[b, g], v[b, g], scale, lim)
+                st = [window_key_start(i, Nq, Nk, window) for i in rows] if window else None
+                o, l = attention_rows(q[b, h, r0:r0 + len(rows)], k[b, g], v[b, g], scale, lim, st)
                 O[b, h, r0:r0 + len(rows)] = o
                 lse[b, h, r0:r0 + len(rows)] = l
     return O, lse
 
 
-def prefill_rows(q, k, v, scale: float, causal: bool, rows):
+def prefill_rows(q, k, v, scale: float, causal: bool, rows, window: int = 0):
     """Selected output rows of a prefill, one by one: ``rows`` is a list of
     (b, h, i).  Returns O (R, d) and LSE (R,).  Used to check full-size runs
     whose whole output the oracle cannot afford."""
@@ -126,7 +146,8 @@ def prefill_rows(q, k, v, scale: float, causal: bool, rows):
     for r, (b, h, i) in enumerate(rows):
         g = kv_head_of(h, Hq, Hkv)
         lim = causal_key_limit(i, Nq, Nk) if causal else Nk
-        o, l = attention_rows(_f64(q[b, h, i:i + 1]), _f64(k[b, g, :lim]), _f64(v[b, g, :lim]), scale)
+        st = window_key_start(i, Nq, Nk, window)
+        o, l = attention_rows(_f64(q[b, h, i:i + 1]), _f64(k[b, g, st:lim]), _f64(v[b, g, st:lim]), scale)
         O[r], lse[r] = o[0], l[0]
     return O, lse
 
@@ -146,8 +167,9 @@ def paged_gather(pool, table_row, L: int, g: int, block_size: int):
     return np.concatenate(out, axis=0)
 
 
-def decode_contiguous(q, k_cache, v_cache, seq_lens, scale: float, heads=None):
-    """One new query per (b, h) against the first L_b cached keys.
+def decode_contiguous(q, k_cache, v_cache, seq_lens, scale: float, heads=None, window: int = 0):
+    """One new query per (b, h) against the first L_b cached keys (the last
+    ``window`` of them when window > 0).
 
     q (B, Hq, d); caches (B, Hkv, S_cap, d).  ``heads`` optionally restricts
     the work to a list of (b, h).  Returns O (B, Hq, d) and LSE (B, Hq) (rows
@@ -161,12 +183,14 @@ def decode_contiguous(q, k_cache, v_cache, seq_lens, scale: float, heads=None):
     for b, h in todo:
         g = kv_head_of(h, Hq, Hkv)
         L = int(lens[b])
-        o, l = attention_rows(_f64(q[b, h:h + 1]), _f64(k_cache[b, g, :L]), _f64(v_cache[b, g, :L]), scale)
+        st = window_key_start(0, 1, L, window)
+        o, l = attention_rows(_f64(q[b, h:h + 1]), _f64(k_cache[b, g, st:L]), _f64(v_cache[b, g, st:L]), scale)
         O[b, h], lse[b, h] = o[0], l[0]
     return O, lse
 
 
-def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int, scale: float, heads=None):
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int, scale: float, heads=None,
+                 window: int = 0):
     """Decode against a paged cache: pools (num_blocks, block_size, Hkv, d),
     block_table (B, max_blocks).  Same outputs as ``decode_contiguous``."""
     B, Hq, d = q.shape
@@ -184,6 +208,7 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int, scal
             cache[(b, g)] = (paged_gather(k_pool, table[b], L, g, block_size),
                              paged_gather(v_pool, table[b], L, g, block_size))
         K, V = cache[(b, g)]
-        o, l = attention_rows(_f64(q[b, h:h + 1]), K, V, scale)
+        st = window_key_start(0, 1, L, window)
+        o, l = attention_rows(_f64(q[b, h:h + 1]), K, V, scale, None, [st])
         O[b, h], lse[b, h] = o[0], l[0]
     return O, lse

@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import _f64, _i64, attention_rows, kv_head_of, paged_gather
+from .attention import _f64, _i64, attention_rows, kv_head_of, paged_gather, window_key_start
 
 
 class BlockAllocator:
@@ -129,7 +129,7 @@ def append_batch_contiguous(k_cache, v_cache, seq_lens, k_new, v_new):
 
 
 def chunked_prefill(q, k_cache, v_cache, seq_lens, scale: float, causal: bool = True,
-                    block_table=None, block_size: int = 0, rows=None):
+                    block_table=None, block_size: int = 0, rows=None, window: int = 0):
     """Attention of the Nq newest tokens of each sequence against its whole
     cache.
 
@@ -137,7 +137,8 @@ def chunked_prefill(q, k_cache, v_cache, seq_lens, scale: float, causal: bool = 
     ``block_table`` is None, else paged pools (num_blocks, block_size, H_kv, d)
     with block_table (B, max_blocks).  ``seq_lens`` (B) count the cached tokens,
     the Nq new ones included (L_b >= Nq when causal).  Query i of sequence b
-    sees keys j < L_b - Nq + i + 1 when causal, all L_b keys otherwise.
+    sees keys j < L_b - Nq + i + 1 when causal, all L_b keys otherwise; with
+    ``window`` W > 0 only keys j > L_b - Nq + i - W besides.
 
     Returns O (B, Hq, Nq, d) and LSE (B, Hq, Nq) in fp64; with ``rows`` (a list
     of (b, h, i)) only those rows, as O (R, d) and LSE (R,).
@@ -162,12 +163,15 @@ def chunked_prefill(q, k_cache, v_cache, seq_lens, scale: float, causal: bool = 
         L = int(lens[b])
         return min(L, max(0, L - Nq + i + 1)) if causal else L
 
+    def start(b, i):
+        return window_key_start(i, Nq, int(lens[b]), window)
+
     if rows is not None:
         O = np.zeros((len(rows), d))
         lse = np.zeros(len(rows))
         for r, (b, h, i) in enumerate(rows):
             K, V = keys(b, kv_head_of(h, Hq, Hkv))
-            o, l = attention_rows(_f64(q[b, h, i:i + 1]), K, V, scale, [limit(b, i)])
+            o, l = attention_rows(_f64(q[b, h, i:i + 1]), K, V, scale, [limit(b, i)], [start(b, i)])
             O[r], lse[r] = o[0], l[0]
         return O, lse
 
@@ -175,8 +179,9 @@ def chunked_prefill(q, k_cache, v_cache, seq_lens, scale: float, causal: bool = 
     lse = np.zeros((B, Hq, Nq))
     for b in range(B):
         lim = [limit(b, i) for i in range(Nq)]
+        st = [start(b, i) for i in range(Nq)]
         for h in range(Hq):
             K, V = keys(b, kv_head_of(h, Hq, Hkv))
-            o, l = attention_rows(_f64(q[b, h]), K, V, scale, lim)
+            o, l = attention_rows(_f64(q[b, h]), K, V, scale, lim, st)
             O[b, h], lse[b, h] = o, l
     return O, lse

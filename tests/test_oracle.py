@@ -379,7 +379,7 @@ def test_mask_alignment_bottom_right_vs_sdpa_top_left():
 # Planted mistakes: each plausible bug in a copy of the oracle fails a pin
 # --------------------------------------------------------------------------
 def _mutant_rows(kind):
-    def rows(q_rows, K, V, scale, key_limits=None):
+    def rows(q_rows, K, V, scale, key_limits=None, key_starts=None):
         q_rows, K, V = A._f64(q_rows), A._f64(K), A._f64(V)
         R, Nk = q_rows.shape[0], K.shape[0]
         S = (q_rows @ K.T) * (1.0 if kind == "no_scale" else scale)
@@ -388,6 +388,8 @@ def _mutant_rows(kind):
             if kind == "mask_off_by_one":
                 lim = lim - 1
             S = np.where(np.arange(Nk)[None, :] < lim, S, -np.inf)
+        if key_starts is not None:
+            S = np.where(np.arange(Nk)[None, :] >= np.asarray(key_starts).reshape(R, 1), S, -np.inf)
         m = S.max(axis=1, keepdims=True)
         E = np.exp(S - m)
         ell = E.sum(axis=1, keepdims=True)

@@ -222,10 +222,10 @@ def test_planted_append_position_is_caught(monkeypatch):
 def test_planted_top_left_chunk_mask_is_caught(monkeypatch):
     real = A.attention_rows
 
-    def top_left(q_rows, K, V, scale, key_limits=None):
+    def top_left(q_rows, K, V, scale, key_limits=None, key_starts=None):
         if key_limits is not None and len(key_limits) > 1:
             key_limits = [i + 1 for i in range(len(key_limits))]
-        return real(q_rows, K, V, scale, key_limits)
+        return real(q_rows, K, V, scale, key_limits, key_starts)
 
     monkeypatch.setattr(PG, "attention_rows", top_left)
     with pytest.raises(AssertionError):
