@@ -15,8 +15,9 @@ Printed: one JSON line.  ``value`` is prefill TFLOP/s (algorithmic flops:
 object holds the decode KV GB/s (algorithmic bytes: every cached K/V byte once,
 plus q, o, lse and the block-table entries read).  Kernel durations come from
 HIP events recorded around each launch on the stream the kernels run on.
-``extras`` (outside the step, skipped with --no-extras) times the KV append
-and the chunked prefill against a paged cache on their own.
+``extras`` (outside the step, skipped with --no-extras) times the KV append,
+the chunked prefill against a paged cache and sliding-window prefill and
+decode, each on its own.
 """
 from __future__ import annotations
 
@@ -96,13 +97,18 @@ def time_launches(fn, steps: int, warmup: int):
     return sum(ms) / steps, ms[steps // 2]
 
 
-def extras(dev, steps: int):
-    """The KV append and the chunked prefill against a paged cache, each on its
-    own: 1024-token chunks of 4 sequences appended to paged caches holding
-    1024..7168 tokens, then attended causally against the whole sequences."""
+def extras(dev, steps: int, dec):
+    """Measurements outside the step, each kernel on its own:
+      * the KV append and the chunked prefill against a paged cache: 1024-token
+        chunks of 4 sequences appended to paged caches holding 1024..7168
+        tokens, then attended causally against the whole sequences;
+      * sliding-window attention (W = 4096): a causal GQA prefill of 32768
+        tokens, and the resident paged decode batch with the window applied.
+    ``dec`` holds the decode batch already in HBM."""
     import torch
     from flashattention_kv_cache_amd import binding
     from flashattention_kv_cache_amd import workloads as W
+    out = {}
     w = W.CHUNKED
     ci = W.chunked_inputs(w)
     q, kn, vn = ci.q.to(dev), ci.k_new.to(dev), ci.v_new.to(dev)
@@ -128,7 +134,7 @@ def extras(dev, steps: int):
     abytes = w.append_bytes() + w.B * 4 + ents * 4
     tf = flops / (c_avg * 1e-3) / 1e12
     gbs = abytes / (a_avg * 1e-3) / 1e9
-    return {
+    out.update({
         "chunked_prefill": {"workload": w.name, "value": round(tf, 3), "unit": "TFLOP/s",
                             "kernel_ms": round(c_avg, 5), "kernel_ms_median": round(c_med, 5), "flops": flops,
                             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
@@ -140,7 +146,48 @@ def extras(dev, steps: int):
                       "kernel_ms_median": round(a_med, 5), "bytes": abytes,
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "kv_append_kernel"}},
-    }
+    })
+    del q, kn, vn, kc, vc, o, lse
+
+    # sliding window: prefill
+    wp = W.WINDOW_PREFILL
+    q, k, v = (t.to(dev) for t in W.prefill_inputs(wp))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    p_avg, p_med = time_launches(lambda: binding.prefill(q, k, v, causal=True, scale=wp.scale, window=wp.window,
+                                                         out=o, lse=lse), steps, 20)
+    tf = wp.flops() / (p_avg * 1e-3) / 1e12
+    out["window_prefill"] = {"workload": wp.name, "value": round(tf, 3), "unit": "TFLOP/s",
+                             "kernel_ms": round(p_avg, 5), "kernel_ms_median": round(p_med, 5), "flops": wp.flops(),
+                             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                          "kernel": "prefill_bf16_kernel<128, contiguous>"}}
+    del q, k, v, o, lse
+
+    # sliding window: decode over the resident batch
+    wd = W.WINDOW_DECODE
+    Wn = wd.window
+    lens = dec["seq_lens_cpu"].to(torch.int64).clamp(max=Wn)
+    first = dec["seq_lens_cpu"].to(torch.int64) - lens
+    ents = int(((first + lens + wd.block_size - 1) // wd.block_size - first // wd.block_size).sum())
+    nbytes = int(lens.sum()) * 2 * wd.Hkv * wd.d * 2 + dec["q"].numel() * 2 * 2 + dec["q"].shape[0] * wd.Hq * 4 \
+        + ents * 4 + wd.B * 4
+    st = binding.decode_split_tokens(wd.B, wd.Hq, wd.Hkv, wd.d, dec["max_seq_len"], Wn)
+    ws = torch.empty(max(1, binding.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.d, dec["max_seq_len"], st, Wn)),
+                     dtype=torch.uint8, device=dev)
+    do = torch.empty_like(dec["q"])
+    dl = torch.empty(dec["q"].shape[:2], dtype=torch.float32, device=dev)
+    d_avg, d_med = time_launches(lambda: binding.decode(dec["q"], dec["k"], dec["v"], dec["lens"],
+                                                        block_table=dec["table"], max_seq_len=dec["max_seq_len"],
+                                                        scale=wd.scale, split_tokens=st, workspace=ws, out=do,
+                                                        lse=dl, window=Wn), steps, 20)
+    gbs = nbytes / (d_avg * 1e-3) / 1e9
+    out["window_decode"] = {"workload": wd.name, "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(d_avg, 5),
+                            "kernel_ms_median": round(d_med, 5), "bytes": nbytes, "split_tokens": st,
+                            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                         "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"}}
+    return out
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -217,6 +264,8 @@ def main():
     nblk_read = int(((di.seq_lens.to(torch.int64) + wd.block_size - 1) // wd.block_size).sum())
     kv_bytes = di.kv_bytes()
     dec_bytes = kv_bytes + dq.numel() * 2 + do.numel() * 2 + dlse.numel() * 4 + nblk_read * 4 + wd.B * 4
+    dec = {"q": dq, "k": dk, "v": dv, "lens": dl, "table": dt_, "max_seq_len": wd.len_hi,
+           "seq_lens_cpu": di.seq_lens.clone()}
     del di
 
     def prefill():
@@ -299,7 +348,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_extras:
-        out["extras"] = extras(dev, max(10, min(K, 50)))
+        out["extras"] = extras(dev, max(10, min(K, 50)), dec)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

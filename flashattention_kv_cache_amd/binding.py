@@ -24,12 +24,12 @@ SIGNATURES = {
     "fa_abi_version": ([], _I),
     "fa_status_string": ([_I], ctypes.c_char_p),
     "fa_last_error": ([], ctypes.c_char_p),
-    "fa_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
-    "fa_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _S),
-    "fa_decode_split_tokens": ([_I, _I, _I, _I, _I], _I),
-    "fa_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P], _I),
+    "fa_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
+    "fa_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _I], _S),
+    "fa_decode_split_tokens": ([_I, _I, _I, _I, _I, _I], _I),
+    "fa_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P], _I),
     "fa_kv_append": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P], _I),
-    "fa_chunked_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
+    "fa_chunked_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -91,9 +91,10 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+            lse: Optional[torch.Tensor] = None, want_lse: bool = True, window: int = 0,
             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """fa_prefill: q (B, Hq, Nq, d), k/v (B, Hkv, Nk, d) -> (o, lse)."""
+    """fa_prefill: q (B, Hq, Nq, d), k/v (B, Hkv, Nk, d) -> (o, lse).
+    ``window`` > 0: causal sliding window of that many keys."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -109,7 +110,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     _check(lib().fa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                            B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                            B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window), float(scale),
                             _dtype_code(q), _stream(stream)))
     return out, lse
 
@@ -171,7 +172,7 @@ def chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                     block_table: Optional[torch.Tensor] = None, block_size: int = 0,
                     max_seq_len: Optional[int] = None, causal: bool = True, scale: Optional[float] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                    want_lse: bool = True, window: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """fa_chunked_prefill: the Nq newest tokens of each sequence, q
     (B, Hq, Nq, d), against its whole cache (contiguous (B, Hkv, S_cap, d) or a
     paged pool with ``block_table``); seq_lens count the cached tokens, the Nq
@@ -190,17 +191,19 @@ def chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     _check(lib().fa_chunked_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
                                     c.block_size, c.max_blocks, c.capacity, int(max_seq_len),
-                                    _ptr(out), _ptr(lse), B, Hq, c.Hkv, Nq, d, int(bool(causal)), float(scale),
+                                    _ptr(out), _ptr(lse), B, Hq, c.Hkv, Nq, d, int(bool(causal)), int(window),
+                                    float(scale),
                                     _dtype_code(q), _stream(stream)))
     return out, lse
 
 
-def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int, split_tokens: int = 0) -> int:
-    return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens))
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int, split_tokens: int = 0,
+                           window: int = 0) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, window, split_tokens))
 
 
-def decode_split_tokens(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int) -> int:
-    return int(lib().fa_decode_split_tokens(B, Hq, Hkv, d, max_seq_len))
+def decode_split_tokens(B: int, Hq: int, Hkv: int, d: int, max_seq_len: int, window: int = 0) -> int:
+    return int(lib().fa_decode_split_tokens(B, Hq, Hkv, d, max_seq_len, window))
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
@@ -208,11 +211,12 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
            max_seq_len: Optional[int] = None, scale: Optional[float] = None,
            split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+           want_lse: bool = True, window: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """fa_decode: q (B, Hq, d) against a contiguous cache (B, Hkv, S_cap, d) or,
     with ``block_table`` (B, max_blocks) int32, a paged pool
     (num_blocks, block_size, Hkv, d).  ``max_seq_len`` bounds seq_lens; it
-    defaults to the capacity of the layout (no device read-back)."""
+    defaults to the capacity of the layout (no device read-back).  ``window``
+    > 0 attends only the last ``window`` keys."""
     B, Hq, d = q.shape
     c = _cache_layout(q, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
     Hkv, paged, block_size, capacity, max_blocks = c.Hkv, c.paged, c.block_size, c.capacity, c.max_blocks
@@ -220,7 +224,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
         max_seq_len = c.bound
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens)
+    need = decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens, window)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
@@ -229,7 +233,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
-                           block_size if paged else 0, max_blocks, capacity, int(max_seq_len),
+                           block_size if paged else 0, max_blocks, capacity, int(max_seq_len), int(window),
                            _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
                            int(split_tokens), _ptr(workspace) if need else None, ws_bytes,
                            _stream(stream)))

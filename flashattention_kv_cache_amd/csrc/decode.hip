@@ -3,7 +3,9 @@
 //
 // What is computed: one new query per (sequence, query head) against every
 // cached key of the sequence, the new token included, no mask ("Генерация и
-// KV-кэш", section "KV-кэш для одной головы на NumPy"); query head h reads KV
+// KV-кэш", section "KV-кэш для одной головы на NumPy") — or, with a sliding
+// window of W keys, against the last W only ("Module 09: Efficient
+// Attention", section "Attention Mask Gallery"); query head h reads KV
 // head floor(h / n_rep) ("Module 09: Efficient Attention", "The Math: Sharing
 // Keys and Values"); paged token t sits at (block_table[t / bs], t % bs) of a
 // (num_blocks, bs, Hkv, d) pool ("Module 09", "Code: A Paged KV Cache from
@@ -104,9 +106,20 @@ __device__ __forceinline__ void keep_loads_here() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ int num_splits(int L, int max_seq_len, int chunk) {
-  if (L < 0 || L > max_seq_len) return 1;  // invalid length: reported by split 0 as NaN
-  return L <= chunk ? 1 : (L + chunk - 1) / chunk;
+// Keys [kbeg, L) of a sequence of L cached tokens: all of them, or the last
+// `window` with a sliding window.  They are cut into splits of `chunk` tokens
+// counted from kbeg.  An invalid length gets one split, which reports it.
+struct KeyRange {
+  int kbeg, ns;
+  bool bad;
+};
+__device__ __forceinline__ KeyRange key_range(int L, const DecodeArgs& a) {
+  KeyRange r;
+  r.bad = L < 0 || L > a.max_seq_len;
+  r.kbeg = (!r.bad && a.window > 0) ? max(0, L - a.window) : 0;
+  const int n = r.bad ? 0 : L - r.kbeg;
+  r.ns = n <= a.split_tokens ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
+  return r;
 }
 
 // Combine running state (m, l, o) with (m2, l2, o2); m are log2-domain maxima.
@@ -142,10 +155,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   const int b = blockIdx.z;
 
   const int L = a.seq_lens[b];
-  const int ns = num_splits(L, a.max_seq_len, a.split_tokens);
+  const KeyRange kr = key_range(L, a);
+  const int ns = kr.ns;
   if (s >= ns) return;
-  bool bad = (L < 0 || L > a.max_seq_len);
-  const int t_begin = bad ? 0 : s * a.split_tokens;
+  bool bad = kr.bad;
+  const int t_begin = bad ? 0 : kr.kbeg + s * a.split_tokens;
   const int t_end = bad ? 0 : min(L, t_begin + a.split_tokens);
 
   const int lane = threadIdx.x & 63;
@@ -356,8 +370,7 @@ template <typename T>
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq;
-  const int L = a.seq_lens[b];
-  const int ns = num_splits(L, a.max_seq_len, a.split_tokens);
+  const int ns = key_range(a.seq_lens[b], a).ns;
   if (ns == 1) return;  // written by the split kernel
   const size_t slot0 = (size_t)bh * a.max_splits;
   float M = -INFINITY;

@@ -90,6 +90,17 @@ int check_cache_layout(const int32_t* block_table, int block_size, int max_block
   return FA_OK;
 }
 
+int check_window(int window, int causal) {
+  if (window < 0) return fail(FA_ERR_INVALID, "window %d must be >= 0 (0 = no window)", window);
+  if (window > 0 && !causal) return fail(FA_ERR_INVALID, "a sliding window needs causal attention");
+  return FA_OK;
+}
+
+// Longest key range a decode query can see: the sliding window caps it.
+int decode_span(int max_seq_len, int window) {
+  return window > 0 && window < max_seq_len ? window : max_seq_len;
+}
+
 int max_splits_for(int max_seq_len, int split_tokens) {
   return max_seq_len <= split_tokens ? 1 : (max_seq_len + split_tokens - 1) / split_tokens;
 }
@@ -98,7 +109,7 @@ int max_splits_for(int max_seq_len, int split_tokens) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 2; }
+int fa_abi_version(void) { return 3; }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
@@ -114,7 +125,7 @@ const char* fa_last_error(void) { return g_err; }
 
 int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d,
-               int causal, float scale, int dtype, void* stream) {
+               int causal, int window, float scale, int dtype, void* stream) {
   if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1)
     return fail(FA_ERR_INVALID, "B=%d Hq=%d Hkv=%d Nq=%d Nk=%d: sizes must be >= 0 and heads >= 1", B, Hq, Hkv, Nq, Nk);
   if (Hq % Hkv) return fail(FA_ERR_INVALID, "num_kv_heads (%d) must divide num_heads (%d)", Hkv, Hq);
@@ -123,6 +134,7 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1, got %d", causal);
   if (causal && Nq > Nk)
     return fail(FA_ERR_INVALID, "causal attention with Nq=%d > Nk=%d would leave rows with no visible key", Nq, Nk);
+  if (check_window(window, causal) != FA_OK) return FA_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
   if (B == 0 || Nq == 0) return ok();
   if (!q || !o || (Nk > 0 && (!k || !v))) return fail(FA_ERR_INVALID, "null tensor pointer");
@@ -131,7 +143,10 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
   const long long rows = (long long)B * Hq * Nq;
   if (rows * d >= (1ll << 40)) return fail(FA_ERR_UNSUPPORTED, "problem too large");
 
-  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  fa::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.causal = causal; a.window = window; a.scale = scale;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = dtype == FA_BF16 ? fa::launch_prefill_bf16(a, st) : fa::launch_prefill_f32(a, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -143,13 +158,14 @@ int fa_chunked_prefill(const void* q, const void* k_cache, const void* v_cache,
                        int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
                        void* o, float* lse,
                        int B, int Hq, int Hkv, int Nq, int d,
-                       int causal, float scale, int dtype, void* stream) {
+                       int causal, int window, float scale, int dtype, void* stream) {
   if (B < 0 || Nq < 0 || Hq < 1 || Hkv < 1)
     return fail(FA_ERR_INVALID, "B=%d Hq=%d Hkv=%d Nq=%d: sizes must be >= 0 and heads >= 1", B, Hq, Hkv, Nq);
   if (Hq % Hkv) return fail(FA_ERR_INVALID, "num_kv_heads (%d) must divide num_heads (%d)", Hkv, Hq);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64 or 128)", d);
   if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (check_window(window, causal) != FA_OK) return FA_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
   int st0 = check_cache_layout(block_table, block_size, max_blocks_per_seq, kv_capacity, max_seq_len);
   if (st0 != FA_OK) return st0;
@@ -166,7 +182,7 @@ int fa_chunked_prefill(const void* q, const void* k_cache, const void* v_cache,
   fa::PrefillArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = 0; a.d = d;
-  a.causal = causal; a.scale = scale;
+  a.causal = causal; a.window = window; a.scale = scale;
   a.seq_lens = seq_lens;
   a.block_table = block_table;
   a.block_size = block_table ? block_size : 0;
@@ -212,15 +228,16 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
   return ok();
 }
 
-int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len) {
-  if (check_decode_sizes(B, Hq, Hkv, d, max_seq_len, 0) != FA_OK) return 0;
-  return choose_split_tokens(B, Hq, Hkv, max_seq_len);
+int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len, int window) {
+  if (check_decode_sizes(B, Hq, Hkv, d, max_seq_len, 0) != FA_OK || window < 0) return 0;
+  return choose_split_tokens(B, Hq, Hkv, decode_span(max_seq_len, window));
 }
 
-size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len, int split_tokens) {
-  if (check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens) != FA_OK) return 0;
-  const int st = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, max_seq_len);
-  const int ns = max_splits_for(max_seq_len, st);
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len, int window, int split_tokens) {
+  if (check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens) != FA_OK || window < 0) return 0;
+  const int span = decode_span(max_seq_len, window);
+  const int st = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, span);
+  const int ns = max_splits_for(span, st);
   if (ns <= 1) return 0;
   const size_t slots = (size_t)B * Hq * ns;
   // partial outputs (d floats per slot) then partial LSEs, each 256-byte aligned
@@ -231,12 +248,13 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len,
 
 int fa_decode(const void* q, const void* k_cache, const void* v_cache,
               const int32_t* seq_lens, const int32_t* block_table,
-              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
               void* o, float* lse,
               int B, int Hq, int Hkv, int d, float scale, int dtype,
               int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   int st0 = check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens);
   if (st0 != FA_OK) return st0;
+  if (check_window(window, 1) != FA_OK) return FA_ERR_INVALID;
   if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
   const bool paged = block_table != nullptr;
@@ -259,9 +277,10 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(FA_ERR_INVALID, "seq_lens and block_table must be 4-byte aligned");
   if (kv_capacity < 1) return fail(FA_ERR_INVALID, "KV capacity must be >= 1");
 
-  const int stoks = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, max_seq_len);
-  const int ns = max_splits_for(max_seq_len, stoks);
-  const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens);
+  const int span = decode_span(max_seq_len, window);
+  const int stoks = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, span);
+  const int ns = max_splits_for(span, stoks);
+  const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, window, split_tokens);
   if (need > 0) {
     if (!workspace) return fail(FA_ERR_INVALID, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
@@ -276,7 +295,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.block_size = paged ? block_size : 0;
   a.log2_block_size = paged ? ilog2(block_size) : 0;
   a.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
-  a.kv_capacity = kv_capacity; a.max_seq_len = max_seq_len;
+  a.kv_capacity = kv_capacity; a.max_seq_len = max_seq_len; a.window = window;
   a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = scale;
   a.split_tokens = stoks; a.max_splits = ns;

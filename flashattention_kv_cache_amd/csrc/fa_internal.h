@@ -17,6 +17,7 @@ struct PrefillArgs {
   float* lse;
   int B, Hq, Hkv, Nq, Nk, d;
   int causal;
+  int window;  // > 0: a causal query sees only its `window` most recent keys
   float scale;
   // Keys read from a KV cache (chunked prefill).  seq_lens == nullptr: plain
   // prefill, Nk keys per head stored (B, Hkv, Nk, d).  Otherwise sequence b has
@@ -49,6 +50,7 @@ struct DecodeArgs {
   const int32_t* block_table;  // nullptr: contiguous layout
   int block_size, log2_block_size, max_blocks_per_seq;
   int kv_capacity, max_seq_len;
+  int window;         // > 0: only the last `window` keys of each sequence
   void* o;
   float* lse;
   int B, Hq, Hkv, d;

@@ -125,12 +125,13 @@ struct TileCopy {
     }
   }
   // Rows [key0, key0 + 64) of one head (src = row 0 of the head) into dst.
-  // Rows at or past Nk are read from row Nk - 1 (harmless: those keys get
-  // weight 0 and the clamped V rows are finite; never out of bounds).
-  __device__ __forceinline__ void copy(const uint16_t* src, const uint16_t* dst_tile, int key0, int Nk, int wave,
-                                       int lane) const {
+  // Rows before klo are read from row klo and rows at or past Nk from row
+  // Nk - 1 (harmless: those keys get weight 0 and the substituted V rows are
+  // finite; rows outside [klo, Nk) are never touched).
+  __device__ __forceinline__ void copy(const uint16_t* src, const uint16_t* dst_tile, int key0, int klo, int Nk,
+                                       int wave, int lane) const {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u16*)dst_tile + (uint32_t)(wave * IPW * RPI * D * 2);
-    if (key0 + kBN <= Nk) {
+    if (key0 >= klo && key0 + kBN <= Nk) {
       const uint16_t* base = src + (size_t)key0 * D;
 #pragma unroll
       for (int i = 0; i < IPW; ++i) lds_dma_saddr(off[i], base, lds0 + i * 1024);
@@ -138,7 +139,7 @@ struct TileCopy {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int row = (wave * IPW + i) * RPI + lane / CPR;
-        const int key = min(key0 + row, Nk - 1);
+        const int key = min(max(key0 + row, klo), Nk - 1);
         const int c = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
         lds_dma_vaddr(src + (size_t)key * D + c * 8, lds0 + i * 1024);
       }
@@ -176,21 +177,22 @@ struct PagedCopy {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) lds_dma_saddr(off[i], base, lds0 + i * 1024);
   }
-  // Any block size, any position: tokens at or past Nk read token Nk - 1.
-  __device__ __forceinline__ void slow(const uint16_t* pool, const int32_t* trow, int key0, int Nk, int lbs,
-                                       int bs, size_t slot_elems, const uint16_t* dst_tile, int wave,
+  // Any block size, any position: tokens before klo read token klo, tokens at
+  // or past Nk read token Nk - 1 (blocks outside [klo, Nk) are never touched).
+  __device__ __forceinline__ void slow(const uint16_t* pool, const int32_t* trow, int key0, int klo, int Nk,
+                                       int lbs, int bs, size_t slot_elems, const uint16_t* dst_tile, int wave,
                                        int lane) const {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u16*)dst_tile + (uint32_t)(wave * IPW * RPI * D * 2);
     int blk[IPW];
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {  // every lookup first: the copies below order memory
-      const int tok = min(key0 + wave * IPW * RPI + i * RPI + lane / CPR, Nk - 1);
+      const int tok = min(max(key0 + wave * IPW * RPI + i * RPI + lane / CPR, klo), Nk - 1);
       blk[i] = trow[tok >> lbs];
     }
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int row = wave * IPW * RPI + i * RPI + lane / CPR;
-      const int tok = min(key0 + row, Nk - 1);
+      const int tok = min(max(key0 + row, klo), Nk - 1);
       const int c = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
       lds_dma_vaddr(pool + ((size_t)blk[i] * bs + (tok & (bs - 1))) * slot_elems + c * 8, lds0 + i * 1024);
     }
@@ -245,26 +247,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   }
   const int off = Nk - a.Nq;
   const int last_row = min(a.Nq, q0 + kBM) - 1;
+  const int W = a.window;  // > 0: sliding window (causal only)
   int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
+  // first key any row of the workgroup sees (its first row's window start)
+  const int kbeg = W > 0 ? max(0, q0 + off - W + 1) : 0;
   if (bad) kend = 0;
+  const int tb = kbeg / kBN;                              // first key tile visited
+  int te = max(tb, (kend + kBN - 1) / kBN);               // one past the last
   const int32_t* trow = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
-  if (PAGED && !bad) {
+  if (PAGED && te > tb) {
     // every token a copy may touch: the visited tiles, clamped to the sequence
-    const int ntok = min(((kend + kBN - 1) / kBN) * kBN, Nk);
+    const int ntok = min(te * kBN, Nk);
+    const int e0 = kbeg >> a.log2_block_size;  // blocks before the first window are never read
     const int ne = (ntok + a.block_size - 1) >> a.log2_block_size;
     int oob = 0;
-    for (int i = threadIdx.x; i < ne; i += kThreads) {
+    for (int i = e0 + threadIdx.x; i < ne; i += kThreads) {
       const int e = trow[i];
       oob |= (e < 0) | (e >= a.kv_capacity);
     }
     if (__syncthreads_or(oob)) {
       bad = true;
-      kend = 0;
+      te = tb;
     }
   }
-  const int n_tiles = (kend + kBN - 1) / kBN;
-  // tiles below this index need no mask for any row of the workgroup
+  // tiles in [n_lo, n_clean) need no mask for any row of the workgroup
   const int n_clean = a.causal ? min((q0 + off + 1) / kBN, Nk / kBN) : Nk / kBN;
+  const int n_lo = W > 0 ? (max(0, last_row + off - W + 1) + kBN - 1) / kBN : 0;
 
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (PAGED ? (size_t)g * D : (size_t)(b * a.Hkv + g) * head_rows * D);
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (PAGED ? (size_t)g * D : (size_t)(b * a.Hkv + g) * head_rows * D);
@@ -302,29 +310,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   }
   // Block id of the first of the 16 tokens this wave copies from tile t
   // (clamped to the sequence; loaded a stage ahead of its use).
-  auto entry = [&](int t) { return trow[min(t * kBN + wave * 16, Nk - 1) >> lbs]; };
+  auto entry = [&](int t) { return trow[min(max(t * kBN + wave * 16, kbeg), Nk - 1) >> lbs]; };
   int eK = 0, eV = 0;  // paged, one_block: block ids for the next stage's K and V copies
   // Tile t of K or V (buffer dst); e = its block id when one_block.
   auto copy_k = [&](uint16_t* dst, int t, int e) {
     if constexpr (PAGED) {
       const int tok0 = t * kBN + wave * 16;
-      if (one_block && tok0 + 16 <= Nk)
+      if (one_block && tok0 >= kbeg && tok0 + 16 <= Nk)
         kcp.fast(kg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
       else
-        kcp.slow(kg, trow, t * kBN, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+        kcp.slow(kg, trow, t * kBN, kbeg, Nk, lbs, bsz, slot_elems, dst, wave, lane);
     } else {
-      kcp.copy(kg, dst, t * kBN, Nk, wave, lane);
+      kcp.copy(kg, dst, t * kBN, kbeg, Nk, wave, lane);
     }
   };
   auto copy_v = [&](uint16_t* dst, int t, int e) {
     if constexpr (PAGED) {
       const int tok0 = t * kBN + wave * 16;
-      if (one_block && tok0 + 16 <= Nk)
+      if (one_block && tok0 >= kbeg && tok0 + 16 <= Nk)
         vcp.fast(vg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
       else
-        vcp.slow(vg, trow, t * kBN, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+        vcp.slow(vg, trow, t * kBN, kbeg, Nk, lbs, bsz, slot_elems, dst, wave, lane);
     } else {
-      vcp.copy(vg, dst, t * kBN, Nk, wave, lane);
+      vcp.copy(vg, dst, t * kBN, kbeg, Nk, wave, lane);
     }
   };
 
@@ -359,13 +367,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // diagonal get weight 0.  Register r of block kb holds key
   // t*64 + kb*32 + 8*(r/4) + 4*hl + r%4, so one compare against a per-lane
   // limit decides each element.
+  // With a window, keys before the row's window start are masked the same way.
   auto mask = [&](f32x16_t (&sacc)[2], int t) {
-    const int lim = (a.causal ? min(qrow + off, Nk - 1) : Nk - 1) - (t * kBN + hl * 4);
+    const int base = t * kBN + hl * 4;
+    const int lim = (a.causal ? min(qrow + off, Nk - 1) : Nk - 1) - base;
+    const int lo = (W > 0 ? qrow + off - W + 1 : 0) - base;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kb * 32 + (r / 4) * 8 + (r % 4) > lim) sacc[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kb * 32 + (r / 4) * 8 + (r % 4);
+        if (kk > lim || kk < lo) sacc[kb][r] = -INFINITY;
+      }
   };
 
   bool pending = false;  // wave-uniform: a rescale of O is due
@@ -391,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
                    bool with_pv) {
     const int kb_next = (t + 1) & 1;  // K(t+1)
-    if (t + 2 < n_tiles) copy_k(sm.k[t & 1], t + 2, eK);
+    if (t + 2 < te) copy_k(sm.k[t & 1], t + 2, eK);
     copy_v(sm.v[t & 1], t, eV);
     if (PAGED && one_block) {
       eK = entry(t + 3);
@@ -411,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
     // ---- running max of tile t; a rescale it calls for applies to l now and
     // to O at the start of the next stage, after PV(t-1).
-    if (t >= n_clean) mask(sc, t);
+    if (t >= n_clean || t < n_lo) mask(sc, t);
     float mx = sc[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
@@ -480,28 +493,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // prologue: K(0) -> K buffer 0, K(1) -> K buffer 1.  The drain is
   // unconditional so that, on every path into the loop, the Q fragments are
   // known to have arrived (otherwise each QK^T MFMA waits on vmcnt).
-  if (n_tiles > 0) {
+  // Tiles are numbered from the start of the sequence; the workgroup visits
+  // [tb, te) and buffer parity follows the tile number.
+  if (te > tb) {
     const bool look = PAGED && one_block;
-    copy_k(sm.k[0], 0, look ? entry(0) : 0);
-    if (n_tiles > 1) copy_k(sm.k[1], 1, look ? entry(1) : 0);
+    copy_k(sm.k[tb & 1], tb, look ? entry(tb) : 0);
+    if (te > tb + 1) copy_k(sm.k[(tb + 1) & 1], tb + 1, look ? entry(tb + 1) : 0);
     if (look) {
-      eK = entry(2);
-      eV = entry(0);
+      eK = entry(tb + 2);
+      eV = entry(tb);
     }
   }
   wait_all_vmem();
   __syncthreads();
-  if (n_tiles > 0) qk(s_a, 0);
-  __syncthreads();  // K buffer 0 is refilled by the first stage
+  if (te > tb) qk(s_a, tb & 1);
+  __syncthreads();  // K buffer of tile tb is refilled by the first stage
 
-  if (n_tiles > 0) {
-    stage(s_a, s_b, p_b, p_a, 0, false);
-    int t = 1;
-    for (; t + 1 < n_tiles; t += 2) {
+  if (te > tb) {
+    stage(s_a, s_b, p_b, p_a, tb, false);
+    int t = tb + 1;
+    for (; t + 1 < te; t += 2) {
       stage(s_b, s_a, p_a, p_b, t, true);
       stage(s_a, s_b, p_b, p_a, t + 1, true);
     }
-    if (t < n_tiles) stage(s_b, s_a, p_a, p_b, t, true);
+    if (t < te) stage(s_b, s_a, p_a, p_b, t, true);
     // drain: a due rescale, then PV of the last tile
     if (pending) {
 #pragma unroll
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
     }
-    if (t < n_tiles) pv(p_b, t & 1);
+    if (t < te) pv(p_b, t & 1);
     else pv(p_a, (t - 1) & 1);
   }
 

@@ -50,17 +50,22 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     if (bad) Nk = 0;
   }
   const int off = Nk - a.Nq;
-  // keys [0, lim) are visible to this row
+  // keys [lo, lim) are visible to this row (lo > 0 only with a sliding window)
   const int lim = a.causal ? min(Nk, row + off + 1) : Nk;
+  const int lo = a.window > 0 ? row + off - a.window + 1 : 0;
   const int last_row = min(a.Nq, (qb + 1) * kRows) - 1;
   int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
   if (bad) kend = 0;
+  // first key any row of the workgroup sees, and the tile it falls in; keys
+  // before klo are never read (their blocks may have been released)
+  const int klo = a.window > 0 ? max(0, qb * kRows + off - a.window + 1) : 0;
+  const int kbeg = (klo / kKeys) * kKeys;
   const int32_t* trow = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
-  if (PAGED && kend > 0) {
+  if (PAGED && kend > kbeg) {
     const int ntok = min(((kend + kKeys - 1) / kKeys) * kKeys, Nk);  // rows the staging loop reads
     const int ne = (ntok + a.block_size - 1) >> a.log2_block_size;
     int oob = 0;
-    for (int i = lane; i < ne; i += 64) {
+    for (int i = (klo >> a.log2_block_size) + lane; i < ne; i += 64) {
       const int e = trow[i];
       oob |= (e < 0) | (e >= a.kv_capacity);
     }
@@ -95,12 +100,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  for (int k0 = 0; k0 < kend; k0 += kKeys) {
-    // stage K and V rows [k0, k0 + kKeys) (zeros past Nk)
+  for (int k0 = kbeg; k0 < kend; k0 += kKeys) {
+    // stage K and V rows [k0, k0 + kKeys) (zeros outside [klo, Nk))
     for (int i = lane; i < kKeys * D / 4; i += 64) {
       const int r = i / (D / 4), cc = i % (D / 4);
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (k0 + r < Nk) {
+      if (k0 + r < Nk && k0 + r >= klo) {
         kv = kv_row(a.k, k0 + r)[cc];
         vv = kv_row(a.v, k0 + r)[cc];
       }
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
           dot = fmaf(qr[e + 2], kk.z, dot);
           dot = fmaf(qr[e + 3], kk.w, dot);
         }
-        s[j] = (k0 + j0 + j < lim) ? dot : -INFINITY;
+        s[j] = (k0 + j0 + j < lim && k0 + j0 + j >= lo) ? dot : -INFINITY;
         mx = fmaxf(mx, s[j]);
       }
       const float m_new = fmaxf(m, mx);

@@ -77,6 +77,7 @@ class PrefillWorkload:
     causal: bool
     dtype: str
     seed: int
+    window: int = 0     # > 0: causal sliding window of that many keys
 
     @property
     def scale(self) -> float:
@@ -87,7 +88,8 @@ class PrefillWorkload:
         if not self.causal:
             return self.Nq * self.Nk
         off = self.Nk - self.Nq
-        return sum(min(self.Nk, i + off + 1) for i in range(self.Nq))
+        W = self.window if self.window > 0 else self.Nk + 1
+        return sum(min(self.Nk, i + off + 1) - max(0, i + off + 1 - W) for i in range(self.Nq))
 
     def flops(self) -> int:
         """2 flop per multiply-add, 2*d MACs per pair (QK^T and PV)."""
@@ -114,6 +116,7 @@ class DecodeWorkload:
     dtype: str
     seed: int
     block_size: int = 16
+    window: int = 0     # > 0: only the last `window` cached keys are attended
 
     @property
     def scale(self) -> float:
@@ -149,11 +152,15 @@ class DecodeInputs:
     def paged(self) -> bool:
         return self.block_table is not None
 
-    def kv_bytes(self) -> int:
-        """Bytes of K and V that a decode step must read: 2*Hkv*d*elem per token."""
+    def kv_bytes(self, window: int = 0) -> int:
+        """Bytes of K and V that a decode step must read: 2*Hkv*d*elem per
+        attended token (the last `window` of each sequence when window > 0)."""
         es = self.k_cache.element_size()
         Hkv, d = self.k_cache.shape[2 if self.paged else 1], self.q.shape[-1]
-        return int(self.seq_lens.to(torch.int64).sum()) * 2 * Hkv * d * es
+        lens = self.seq_lens.to(torch.int64)
+        if window > 0:
+            lens = lens.clamp(max=window)
+        return int(lens.sum()) * 2 * Hkv * d * es
 
 
 def decode_inputs(w: DecodeWorkload) -> DecodeInputs:
@@ -348,3 +355,13 @@ def chunked_inputs(w: ChunkedWorkload) -> ChunkedInputs:
 # hold 1024..7168 tokens (the prefill half of a chunked-prefill serving step).
 CHUNKED = ChunkedWorkload("chunked prefill bf16 vs paged cache, B=4 Hq=32 Hkv=8 d=128 chunk=1024 "
                           "past~U[1024,7168] bs=16", 4, 32, 8, 128, 1024, 1024, 7168, 16, "bf16", 1005)
+
+
+# Sliding-window attention (a window of 4096 keys, Mistral-style): a long causal
+# GQA prefill, and the paged decode batch above (same seed, so the same cache)
+# with the window applied.
+WINDOW_PREFILL = PrefillWorkload("sliding-window causal GQA prefill bf16, Hq=32 Hkv=8 N=32768 d=128 W=4096",
+                                 1, 32, 8, 32768, 32768, 128, True, "bf16", 1006, window=4096)
+WINDOW_DECODE = DecodeWorkload("sliding-window paged decode bf16, B=128 Hq=32 Hkv=8 d=128 bs=16 "
+                               "L~U[512,32768] W=4096", 128, 32, 8, 128, 512, 32768, True, "bf16", 1004,
+                               window=4096)

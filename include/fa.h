@@ -80,30 +80,37 @@ const char* fa_last_error(void);
  *                         bottom-right corner so that Nq new queries appended to
  *                         Nk - Nq cached keys see the whole past ("Генерация и
  *                         KV-кэш", section "Три ловушки", item 2)
+ *   window                0: no window.  W > 0 (causal only): query i sees
+ *                         only keys j > i + (Nk - Nq) - W, i.e. its W most
+ *                         recent keys, itself included — the sliding-window
+ *                         mask of "Module 09: Efficient Attention", section
+ *                         "Attention Mask Gallery"; the work per query is
+ *                         then O(W) instead of O(Nk)
  *
  * Contract: B, Nq, Nk >= 0; Hq, Hkv >= 1; Hq % Hkv == 0; d in {64, 128};
- * causal requires Nq <= Nk (otherwise rows with no visible key would exist).
+ * causal requires Nq <= Nk (otherwise rows with no visible key would exist);
+ * window >= 0, and window > 0 requires causal.
  * Nk == 0 (non-causal) yields o = 0 and lse = -inf.  B == 0 or Nq == 0 is a
  * no-op.  q, k, v must not alias o or lse.
  */
 int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d,
-               int causal, float scale, int dtype, void* stream);
+               int causal, int window, float scale, int dtype, void* stream);
 
 /*
  * fa_decode_workspace_bytes — bytes of device workspace fa_decode needs for
- * these sizes (0 when every sequence fits in one split).  `split_tokens` is
- * the same value that will be passed to fa_decode (0 = library choice).
- * Returns 0 for arguments fa_decode would reject.
+ * these sizes (0 when every sequence fits in one split).  `window` and
+ * `split_tokens` are the values that will be passed to fa_decode (0 = no
+ * window / library choice).  Returns 0 for arguments fa_decode would reject.
  */
-size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len,
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len, int window,
                                  int split_tokens);
 
 /*
  * fa_decode_split_tokens — tokens per split that fa_decode uses for these
  * sizes when called with split_tokens = 0.
  */
-int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len);
+int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len, int window);
 
 /*
  * fa_decode — one new query per (sequence, query head) against all of that
@@ -134,6 +141,11 @@ int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len);
  *   kv_capacity  contiguous: S_cap (>= max_seq_len); paged: pool blocks
  *   max_seq_len  host-side upper bound on every L_b (sizes the launch without
  *                reading seq_lens back)
+ *   window       0, or W > 0: only the last W cached keys of each sequence
+ *                are attended (the sliding window of "Module 09: Efficient
+ *                Attention", section "Attention Mask Gallery"); the blocks
+ *                before them are not read, so their table entries may be
+ *                stale or -1
  *   o            (B, Hq, d) output, input dtype
  *   lse          (B, Hq) fp32 output or NULL
  *   split_tokens 0 = library choice, else tokens per split: a multiple of 256
@@ -149,7 +161,7 @@ int fa_decode_split_tokens(int B, int Hq, int Hkv, int d, int max_seq_len);
  */
 int fa_decode(const void* q, const void* k_cache, const void* v_cache,
               const int32_t* seq_lens, const int32_t* block_table,
-              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
               void* o, float* lse,
               int B, int Hq, int Hkv, int d, float scale, int dtype,
               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
@@ -210,8 +222,10 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
  *   o            (B, Hq, Nq, d) output, input dtype
  *   lse          (B, Hq, Nq) fp32 output or NULL (as for fa_prefill)
  *   causal       1 for a prompt chunk; 0 lets every query see all L_b keys
+ *   window       as fa_prefill (positions counted in the whole sequence); the
+ *                blocks before the first window of the chunk are not read
  *
- * Contract: as fa_prefill for B, heads, d, scale; 0 <= L_b <= max_seq_len and,
+ * Contract: as fa_prefill for B, heads, d, scale, window; 0 <= L_b <= max_seq_len and,
  * when causal, L_b >= Nq; contiguous kv_capacity >= max_seq_len; paged:
  * block_size a power of two in [1, 1024], max_blocks_per_seq * block_size >=
  * max_seq_len and every block id read in [0, kv_capacity).  Device-side
@@ -224,7 +238,7 @@ int fa_chunked_prefill(const void* q, const void* k_cache, const void* v_cache,
                        int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
                        void* o, float* lse,
                        int B, int Hq, int Hkv, int Nq, int d,
-                       int causal, float scale, int dtype, void* stream);
+                       int causal, int window, float scale, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(fa):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(fa.SIGNATURES) == set(declared_functions())
-    assert L.fa_abi_version() == 2
+    assert L.fa_abi_version() == 3
 
 
 def test_status_strings(fa):
@@ -45,9 +45,11 @@ def test_status_strings(fa):
     assert "HIP" in fa.status_string(FA_ERR_HIP)
 
 
-def prefill(fa, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, causal=1, scale=0.125, dtype=BF16):
+def prefill(fa, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, causal=1, window=0, scale=0.125,
+            dtype=BF16):
     P = ctypes.c_void_p
-    return fa.lib().fa_prefill(P(q), P(k), P(v), P(o), P(lse), B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, None)
+    return fa.lib().fa_prefill(P(q), P(k), P(v), P(o), P(lse), B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                               None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -59,6 +61,8 @@ def prefill(fa, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, c
     (dict(dtype=7), FA_ERR_INVALID, "dtype"),
     (dict(causal=2), FA_ERR_INVALID, "causal"),
     (dict(Nq=9, Nk=8), FA_ERR_INVALID, "Nq=9 > Nk=8"),
+    (dict(window=-1), FA_ERR_INVALID, "window"),
+    (dict(window=4, causal=0), FA_ERR_INVALID, "sliding window needs causal"),
     (dict(scale=0.0), FA_ERR_INVALID, "scale"),
     (dict(scale=float("inf")), FA_ERR_INVALID, "scale"),
     (dict(scale=float("nan")), FA_ERR_INVALID, "scale"),
@@ -79,10 +83,10 @@ def test_prefill_empty_is_a_noop(fa):
     assert fa.lib().fa_last_error().decode() == ""
 
 
-def decode(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, o=A, lse=A,
+def decode(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, window=0, o=A, lse=A,
            B=2, Hq=8, Hkv=2, d=128, scale=0.1, dtype=BF16, split=0, ws=None, ws_bytes=0):
     P = ctypes.c_void_p
-    return fa.lib().fa_decode(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, P(o), P(lse),
+    return fa.lib().fa_decode(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, window, P(o), P(lse),
                               B, Hq, Hkv, d, scale, dtype, split, P(ws), ws_bytes, None)
 
 
@@ -93,6 +97,7 @@ def decode(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=
     (dict(scale=-1.0), FA_ERR_INVALID, "scale"),
     (dict(split=100), FA_ERR_INVALID, "multiple of 256"),
     (dict(maxlen=-1), FA_ERR_INVALID, "max_seq_len"),
+    (dict(window=-3), FA_ERR_INVALID, "window"),
     (dict(cap=32, maxlen=64), FA_ERR_INVALID, "capacity"),                 # contiguous S_cap < max len
     (dict(table=A, bs=12), FA_ERR_INVALID, "power of two"),
     (dict(table=A, bs=2048, mbps=1), FA_ERR_INVALID, "power of two"),
@@ -113,8 +118,8 @@ def test_decode_rejects(fa, kw, status, msg):
 def test_decode_workspace_contract(fa):
     L = fa.lib()
     # one split per sequence needs no workspace
-    assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 256, 256) == 0
-    n = L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 256)
+    assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 256, 0, 256) == 0
+    n = L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 0, 256)
     slots = 2 * 8 * 4
     assert n == ((slots * 128 * 4 + 255) // 256) * 256 + ((slots * 4 + 255) // 256) * 256
     # a call that needs it without one, or with too little, is rejected
@@ -123,15 +128,22 @@ def test_decode_workspace_contract(fa):
     assert decode(fa, maxlen=1024, cap=1024, split=256, ws=A, ws_bytes=n - 1) == FA_ERR_INVALID
     assert decode(fa, maxlen=1024, cap=1024, split=256, ws=A + 16, ws_bytes=n) == FA_ERR_INVALID
     # rejected sizes report 0
-    assert L.fa_decode_workspace_bytes(2, 8, 3, 128, 1024, 0) == 0
+    assert L.fa_decode_workspace_bytes(2, 8, 3, 128, 1024, 0, 0) == 0
+    assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, -1, 0) == 0
+    # a window caps the keys a query sees, and with them the splits
+    assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 256, 256) == 0
+    assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 512, 256) == \
+        ((2 * 8 * 2 * 128 * 4 + 255) // 256) * 256 + 256
 
 
 def test_decode_split_choice(fa):
     L = fa.lib()
     for args in [(64, 32, 8, 128, 8192), (128, 32, 8, 128, 32768), (1, 32, 8, 128, 4096), (4, 8, 8, 64, 100)]:
-        st = L.fa_decode_split_tokens(*args)
+        st = L.fa_decode_split_tokens(*args, 0)
         assert st >= 256 and st % 256 == 0 and st <= 4096
-    assert L.fa_decode_split_tokens(2, 8, 3, 128, 100) == 0
+    assert L.fa_decode_split_tokens(2, 8, 3, 128, 100, 0) == 0
+    # a window shorter than the longest sequence sizes the splits by the window
+    assert L.fa_decode_split_tokens(128, 32, 8, 128, 32768, 1024) == L.fa_decode_split_tokens(128, 32, 8, 128, 1024, 0)
 
 
 def test_decode_empty_batch_is_a_noop(fa):
@@ -139,10 +151,10 @@ def test_decode_empty_batch_is_a_noop(fa):
 
 
 def chunked(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, o=A, lse=A,
-            B=2, Hq=8, Hkv=2, Nq=16, d=128, causal=1, scale=0.1, dtype=BF16):
+            B=2, Hq=8, Hkv=2, Nq=16, d=128, causal=1, window=0, scale=0.1, dtype=BF16):
     P = ctypes.c_void_p
     return fa.lib().fa_chunked_prefill(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, P(o), P(lse),
-                                       B, Hq, Hkv, Nq, d, causal, scale, dtype, None)
+                                       B, Hq, Hkv, Nq, d, causal, window, scale, dtype, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -151,6 +163,8 @@ def chunked(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen
     (dict(d=96), FA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=9), FA_ERR_INVALID, "dtype"),
     (dict(causal=3), FA_ERR_INVALID, "causal"),
+    (dict(window=-1), FA_ERR_INVALID, "window"),
+    (dict(window=8, causal=0), FA_ERR_INVALID, "sliding window needs causal"),
     (dict(scale=0.0), FA_ERR_INVALID, "scale"),
     (dict(maxlen=-1), FA_ERR_INVALID, "max_seq_len"),
     (dict(Nq=65, maxlen=64), FA_ERR_INVALID, "exceeds max_seq_len"),
