@@ -139,7 +139,7 @@ def extras(dev, steps: int, dec):
                             "kernel_ms": round(c_avg, 5), "kernel_ms_median": round(c_med, 5), "flops": flops,
                             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                         "kernel": "prefill_bf16_kernel<128, paged>"}},
+                                         "kernel": "prefill_bf16_kernel<128, paged, no window>"}},
         "kv_append": {"workload": f"append of the same chunks ({w.B} x {w.chunk} tokens, {w.Hkv} KV heads, "
                                   f"d={w.d}, bf16) into the paged pool",
                       "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(a_avg, 5),
@@ -161,7 +161,7 @@ def extras(dev, steps: int, dec):
                              "kernel_ms": round(p_avg, 5), "kernel_ms_median": round(p_med, 5), "flops": wp.flops(),
                              "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                           "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                          "kernel": "prefill_bf16_kernel<128, contiguous>"}}
+                                          "kernel": "prefill_bf16_kernel<128, contiguous, no window>"}}
     del q, k, v, o, lse
 
     # sliding window: decode over the resident batch
@@ -340,7 +340,7 @@ def main():
                    "kernel_ms_median": round(dec_ms[K // 2], 5), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill"),
-                     "algorithmic_bytes": wp.algorithmic_bytes(), "kernel": "prefill_bf16_kernel<128, contiguous>"},
+                     "algorithmic_bytes": wp.algorithmic_bytes(), "kernel": "prefill_bf16_kernel<128, contiguous, no window>"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                             "algorithmic_bytes": dec_bytes,

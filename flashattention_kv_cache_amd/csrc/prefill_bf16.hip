@@ -199,7 +199,7 @@ struct PagedCopy {
   }
 };
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool WINDOW>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb) {
   __shared__ Smem<D> sm;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   }
   const int off = Nk - a.Nq;
   const int last_row = min(a.Nq, q0 + kBM) - 1;
-  const int W = a.window;  // > 0: sliding window (causal only)
+  const int W = WINDOW ? a.window : 0;  // > 0: sliding window (causal only)
   int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
   // first key any row of the workgroup sees (its first row's window start)
   const int kbeg = W > 0 ? max(0, q0 + off - W + 1) : 0;
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = kb * 32 + (r / 4) * 8 + (r % 4);
-        if (kk > lim || kk < lo) sacc[kb][r] = -INFINITY;
+        if (kk > lim || (WINDOW && kk < lo)) sacc[kb][r] = -INFINITY;
       }
   };
 
@@ -553,14 +553,17 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.Nq + kBM - 1) / kBM;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const bool paged = a.block_table != nullptr;
+  const bool paged = a.block_table != nullptr, win = a.window > 0;
+#define FA_LAUNCH(DD, PG, WN) \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, PG, WN>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb)
   if (a.d == 64) {
-    if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+    if (paged) { if (win) FA_LAUNCH(64, true, true); else FA_LAUNCH(64, true, false); }
+    else { if (win) FA_LAUNCH(64, false, true); else FA_LAUNCH(64, false, false); }
   } else {
-    if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb);
+    if (paged) { if (win) FA_LAUNCH(128, true, true); else FA_LAUNCH(128, true, false); }
+    else { if (win) FA_LAUNCH(128, false, true); else FA_LAUNCH(128, false, false); }
   }
+#undef FA_LAUNCH
   return hipGetLastError();
 }
 
