@@ -161,7 +161,7 @@ def extras(dev, steps: int, dec):
                              "kernel_ms": round(p_avg, 5), "kernel_ms_median": round(p_med, 5), "flops": wp.flops(),
                              "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                           "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                          "kernel": "prefill_bf16_kernel<128, contiguous, no window>"}}
+                                          "kernel": "prefill_bf16_kernel<128, contiguous, window>"}}
     del q, k, v, o, lse
 
     # sliding window: decode over the resident batch
