@@ -31,14 +31,22 @@ from typing import Optional
 
 import torch
 
-_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+# FP8 caches hold the E4M3 codes of N(0, 1) draws times FP8_SIGMA (magnitudes up
+# to ~5 sigma = 320 stay below E4M3's 448); FP8_SCALE = 1 / FP8_SIGMA is the
+# per-tensor scale that maps the codes back to unit variance.
+FP8_SIGMA = 64.0
+FP8_SCALE = 1.0 / FP8_SIGMA
+FP8_NAN = 0x7F           # an E4M3 NaN code: the poison of unowned FP8 slots
 
 
 _CHUNK = 1 << 24  # elements per independently seeded chunk
 
 
 def _normal(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
-    """N(0,1) fp32 draws rounded to ``dtype``.
+    """N(0,1) fp32 draws rounded to ``dtype`` ("fp8": E4M3 codes, as uint8, of
+    the draws times FP8_SIGMA, rounded to nearest even by PyTorch's cast).
 
     One 62-bit base seed is drawn from ``gen``; element chunk c (of a fixed
     2^24 elements) is drawn from a fresh generator seeded base + c.  The values
@@ -52,7 +60,11 @@ def _normal(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
     def fill(c: int):
         s, e = c * _CHUNK, min(n, (c + 1) * _CHUNK)
         g = torch.Generator().manual_seed(base + c)
-        out[s:e] = torch.randn(e - s, generator=g, dtype=torch.float32).to(out.dtype)
+        x = torch.randn(e - s, generator=g, dtype=torch.float32)
+        if dtype == "fp8":
+            out[s:e] = (x * FP8_SIGMA).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            out[s:e] = x.to(out.dtype)
 
     nchunks = (n + _CHUNK - 1) // _CHUNK
     if nchunks <= 1:
@@ -155,7 +167,7 @@ class DecodeInputs:
     def kv_bytes(self, window: int = 0) -> int:
         """Bytes of K and V that a decode step must read: 2*Hkv*d*elem per
         attended token (the last `window` of each sequence when window > 0)."""
-        es = self.k_cache.element_size()
+        es = self.k_cache.element_size()   # 1 for an FP8 cache
         Hkv, d = self.k_cache.shape[2 if self.paged else 1], self.q.shape[-1]
         lens = self.seq_lens.to(torch.int64)
         if window > 0:
@@ -174,7 +186,8 @@ def make_decode_inputs(B, Hq, Hkv, d, dtype, seed, len_range=None, seq_lens=None
                        max_blocks: Optional[int] = None, spare_blocks: int = 0) -> DecodeInputs:
     """Give either ``len_range=(lo, hi)`` (lengths drawn uniformly, inclusive)
     or ``seq_lens`` (B explicit lengths).  ``spare_blocks`` adds pool blocks
-    that no sequence owns (all NaN)."""
+    that no sequence owns (all NaN).  dtype "fp8": bf16 queries, E4M3 caches
+    (codes as uint8, scale FP8_SCALE)."""
     g = torch.Generator().manual_seed(seed)
     if seq_lens is None:
         lo, hi = len_range
@@ -184,15 +197,16 @@ def make_decode_inputs(B, Hq, Hkv, d, dtype, seed, len_range=None, seq_lens=None
         seq_lens = torch.tensor(list(seq_lens), dtype=torch.int64)
         assert seq_lens.numel() == B
         max_seq_len = int(seq_lens.max()) if B > 0 else 0
-    q = _normal(g, (B, Hq, d), dtype)
+    q = _normal(g, (B, Hq, d), "bf16" if dtype == "fp8" else dtype)
+    poison = FP8_NAN if dtype == "fp8" else float("nan")
     if not paged:
         cap = s_cap if s_cap is not None else max_seq_len
         k = _normal(g, (B, Hkv, cap, d), dtype)
         v = _normal(g, (B, Hkv, cap, d), dtype)
         for b in range(B):
             L = int(seq_lens[b])
-            k[b, :, L:, :] = float("nan")
-            v[b, :, L:, :] = float("nan")
+            k[b, :, L:, :] = poison
+            v[b, :, L:, :] = poison
         return DecodeInputs(q, k, v, seq_lens.to(torch.int32), None, 0, cap, max_seq_len)
     bs = block_size
     nblk = [(int(L) + bs - 1) // bs for L in seq_lens]
@@ -210,11 +224,11 @@ def make_decode_inputs(B, Hq, Hkv, d, dtype, seed, len_range=None, seq_lens=None
         L = int(seq_lens[b])
         if L % bs:
             last = int(table[b, nblk[b] - 1])
-            k[last, L % bs:] = float("nan")
-            v[last, L % bs:] = float("nan")
+            k[last, L % bs:] = poison
+            v[last, L % bs:] = poison
     for p in perm[sum(nblk):].tolist():      # spare blocks nobody owns
-        k[p] = float("nan")
-        v[p] = float("nan")
+        k[p] = poison
+        v[p] = poison
     return DecodeInputs(q, k, v, seq_lens.to(torch.int32), table, bs, total, max_seq_len)
 
 
@@ -365,3 +379,8 @@ WINDOW_PREFILL = PrefillWorkload("sliding-window causal GQA prefill bf16, Hq=32 
 WINDOW_DECODE = DecodeWorkload("sliding-window paged decode bf16, B=128 Hq=32 Hkv=8 d=128 bs=16 "
                                "L~U[512,32768] W=4096", 128, 32, 8, 128, 512, 32768, True, "bf16", 1004,
                                window=4096)
+
+# The paged decode batch above with an FP8 (E4M3) cache: same lengths and block
+# table (same seed), one byte per cached number.
+FP8_DECODE = DecodeWorkload("paged decode, bf16 queries, FP8 E4M3 cache, B=128 Hq=32 Hkv=8 d=128 bs=16 "
+                            "L~U[512,32768]", 128, 32, 8, 128, 512, 32768, True, "fp8", 1004)

@@ -17,6 +17,9 @@ Modules:
   paged      the paged pool: free-list block allocation, token append through
              the block table, prefix sharing, and chunked prefill (the newest
              Nq tokens of each sequence against its whole cache).
+  fp8        FP8 (E4M3) caches: the code -> value table from the bit layout,
+             round-to-nearest-even quantisation with saturation, per-tensor
+             scales, decode against an FP8 cache, quantising append.
 
 Every function cites the passage it follows by page title and section.  All
 functions are pinned by tests that check them against values the pages print,
@@ -28,6 +31,7 @@ from .online import online_softmax_stats, online_attention_row, merge_partials
 from .kv_bytes import kv_cache_bytes, kv_bytes_per_token
 from .paged import (BlockAllocator, PagedSequence, append_token, share_prefix, append_batch,
                     append_batch_contiguous, chunked_prefill)
+from .fp8 import e4m3_value, decode_codes, quantize_e4m3, decode_fp8, append_fp8
 
 __all__ = [
     "kv_head_of", "causal_key_limit", "window_key_start", "attention_rows", "prefill", "prefill_rows",
@@ -36,4 +40,5 @@ __all__ = [
     "kv_cache_bytes", "kv_bytes_per_token",
     "BlockAllocator", "PagedSequence", "append_token", "share_prefix", "append_batch",
     "append_batch_contiguous", "chunked_prefill",
+    "e4m3_value", "decode_codes", "quantize_e4m3", "decode_fp8", "append_fp8",
 ]
