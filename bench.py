@@ -16,8 +16,8 @@ object holds the decode KV GB/s (algorithmic bytes: every cached K/V byte once,
 plus q, o, lse and the block-table entries read).  Kernel durations come from
 HIP events recorded around each launch on the stream the kernels run on.
 ``extras`` (outside the step, skipped with --no-extras) times the KV append,
-the chunked prefill against a paged cache and sliding-window prefill and
-decode, each on its own.
+the chunked prefill against a paged cache, sliding-window prefill and decode,
+and decode against an FP8 cache, each on its own.
 """
 from __future__ import annotations
 
@@ -182,11 +182,40 @@ def extras(dev, steps: int, dec):
                                                         scale=wd.scale, split_tokens=st, workspace=ws, out=do,
                                                         lse=dl, window=Wn), steps, 20)
     gbs = nbytes / (d_avg * 1e-3) / 1e9
-    out["window_decode"] = {"workload": wd.name, "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(d_avg, 5),
+    out_window = {"workload": wd.name, "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(d_avg, 5),
                             "kernel_ms_median": round(d_med, 5), "bytes": nbytes, "split_tokens": st,
                             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                          "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"}}
+    out["window_decode"] = out_window
+
+    # FP8 (E4M3) cache: the resident batch's cache rounded to E4M3 codes on the
+    # GPU (times 64, scale 1/64), same lengths and block table
+    wf = W.FP8_DECODE
+    fk = torch.empty(dec["k"].shape, dtype=torch.uint8, device=dev)
+    fv = torch.empty_like(fk)
+    step = 4096
+    for i in range(0, fk.shape[0], step):
+        fk[i:i + step] = (dec["k"][i:i + step].float() * W.FP8_SIGMA).to(torch.float8_e4m3fn).view(torch.uint8)
+        fv[i:i + step] = (dec["v"][i:i + step].float() * W.FP8_SIGMA).to(torch.float8_e4m3fn).view(torch.uint8)
+    tokens = int(dec["seq_lens_cpu"].to(torch.int64).sum())
+    nblk = int(((dec["seq_lens_cpu"].to(torch.int64) + wf.block_size - 1) // wf.block_size).sum())
+    fbytes = tokens * 2 * wf.Hkv * wf.d + dec["q"].numel() * 2 * 2 + wf.B * wf.Hq * 4 + nblk * 4 + wf.B * 4
+    st = binding.decode_split_tokens(wf.B, wf.Hq, wf.Hkv, wf.d, dec["max_seq_len"])
+    ws = torch.empty(max(1, binding.decode_workspace_bytes(wf.B, wf.Hq, wf.Hkv, wf.d, dec["max_seq_len"], st)),
+                     dtype=torch.uint8, device=dev)
+    f_avg, f_med = time_launches(lambda: binding.decode_fp8(dec["q"], fk, fv, dec["lens"], W.FP8_SCALE, W.FP8_SCALE,
+                                                            block_table=dec["table"], max_seq_len=dec["max_seq_len"],
+                                                            scale=wf.scale, split_tokens=st, workspace=ws, out=do,
+                                                            lse=dl), steps, 20)
+    gbs = fbytes / (f_avg * 1e-3) / 1e9
+    out["fp8_decode"] = {"workload": wf.name, "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(f_avg, 5),
+                         "kernel_ms_median": round(f_med, 5), "bytes": fbytes, "split_tokens": st,
+                         "tokens_per_s": round(tokens / (f_avg * 1e-3), 1),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                      "kernel": "decode_split_kernel<fp8,128,4,paged> + decode_merge_kernel"}}
+    del fk, fv
     return out
 
 

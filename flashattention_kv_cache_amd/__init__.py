@@ -1,12 +1,13 @@
 """Exact softmax attention for AMD Instinct MI355X (gfx950).
 
-``prefill``, ``decode``, ``chunked_prefill`` and ``kv_append`` call the C-ABI
+``prefill``, ``decode`` (``decode_fp8``), ``chunked_prefill`` and ``kv_append``
+(``kv_append_fp8``) call the C-ABI
 library libfa.so (include/fa.h), whose hand-written HIP kernels do all of the
 arithmetic; PyTorch supplies device memory and streams.  ``workloads`` holds
 the seeded synthetic inputs.
 """
-from .binding import (FAError, chunked_prefill, decode, decode_split_tokens,  # noqa: F401
-                      decode_workspace_bytes, kv_append, lib, prefill)
+from .binding import (FAError, chunked_prefill, decode, decode_fp8, decode_split_tokens,  # noqa: F401
+                      decode_workspace_bytes, kv_append, kv_append_fp8, lib, prefill)
 
-__all__ = ["prefill", "decode", "chunked_prefill", "kv_append", "decode_workspace_bytes",
-           "decode_split_tokens", "FAError", "lib"]
+__all__ = ["prefill", "decode", "decode_fp8", "chunked_prefill", "kv_append", "kv_append_fp8",
+           "decode_workspace_bytes", "decode_split_tokens", "FAError", "lib"]

@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P], _I),
     "fa_kv_append": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P], _I),
     "fa_chunked_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
+    "fa_decode_fp8": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _F, _F, _I, _P, _S, _P], _I),
+    "fa_kv_append_fp8": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P], _I),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -123,7 +125,7 @@ class _Cache:
         self.capacity, self.max_blocks, self.bound = capacity, max_blocks, bound
 
 
-def _cache_layout(ref, k_cache, v_cache, seq_lens, block_table, block_size, B, d) -> _Cache:
+def _cache_layout(ref, k_cache, v_cache, seq_lens, block_table, block_size, B, d, cache_dtype=None) -> _Cache:
     """Check a contiguous cache (B, Hkv, S_cap, d) or a paged pool
     (num_blocks, block_size, Hkv, d) with its block table (B, max_blocks)."""
     for t, n in ((ref, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
@@ -145,9 +147,68 @@ def _cache_layout(ref, k_cache, v_cache, seq_lens, block_table, block_size, B, d
         if Bc != B:
             raise ValueError("cache batch != q batch")
         c = _Cache(Hkv, False, 0, cap, 0, cap)
-    if dk != d or v_cache.shape != k_cache.shape or k_cache.dtype != ref.dtype or v_cache.dtype != ref.dtype:
+    want = ref.dtype if cache_dtype is None else cache_dtype
+    if dk != d or v_cache.shape != k_cache.shape or k_cache.dtype != want or v_cache.dtype != want:
         raise ValueError("inputs and caches disagree in head dim, shape or dtype")
     return c
+
+
+def _fp8_cache(t: torch.Tensor) -> torch.Tensor:
+    """E4M3 caches are passed as uint8 codes or as torch.float8_e4m3fn."""
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+               k_scale: float, v_scale: float, block_table: Optional[torch.Tensor] = None, block_size: int = 0,
+               max_seq_len: Optional[int] = None, scale: Optional[float] = None, split_tokens: int = 0,
+               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True, window: int = 0,
+               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fa_decode_fp8: bf16 q (B, Hq, d) against an FP8 E4M3 cache (uint8 codes
+    or float8_e4m3fn), contiguous or paged as for ``decode``; a code stands
+    for value(code) * k_scale (keys) or * v_scale (values)."""
+    k_cache, v_cache = _fp8_cache(k_cache), _fp8_cache(v_cache)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("fa_decode_fp8 takes bf16 queries")
+    B, Hq, d = q.shape
+    c = _cache_layout(q, k_cache, v_cache, seq_lens, block_table, block_size, B, d, torch.uint8)
+    if max_seq_len is None:
+        max_seq_len = c.bound
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, Hq, c.Hkv, d, max_seq_len, split_tokens, window)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+                               c.block_size, c.max_blocks, c.capacity, int(max_seq_len), int(window),
+                               _ptr(out), _ptr(lse), B, Hq, c.Hkv, d, float(scale), float(k_scale),
+                               float(v_scale), int(split_tokens), _ptr(workspace) if need else None, ws_bytes,
+                               _stream(stream)))
+    return out, lse
+
+
+def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  seq_lens: torch.Tensor, k_scale: float, v_scale: float,
+                  block_table: Optional[torch.Tensor] = None, block_size: int = 0, stream=None) -> None:
+    """fa_kv_append_fp8: quantise bf16 k_new/v_new (B, Hkv, n_new, d) into an
+    FP8 E4M3 cache at positions seq_lens[b] - n_new .. seq_lens[b] - 1."""
+    k_cache, v_cache = _fp8_cache(k_cache), _fp8_cache(v_cache)
+    _dev(v_new, "v_new")
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or k_new.dtype != torch.bfloat16 or \
+            v_new.dtype != torch.bfloat16:
+        raise ValueError("expected bf16 k_new, v_new (B, Hkv, n_new, d)")
+    B, Hkv, n_new, d = k_new.shape
+    c = _cache_layout(k_new, k_cache, v_cache, seq_lens, block_table, block_size, B, d, torch.uint8)
+    if c.Hkv != Hkv:
+        raise ValueError("new rows and cache disagree in KV heads")
+    _check(lib().fa_kv_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                  _ptr(block_table), c.block_size, c.max_blocks, c.capacity,
+                                  B, Hkv, n_new, d, float(k_scale), float(v_scale), _stream(stream)))
 
 
 def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -31,6 +31,8 @@
 //     workspace and a second kernel merges a sequence's splits with weights
 //     exp(lse_s - max lse) — the same recurrence applied to whole splits.  A
 //     sequence that fits in one split is written directly.
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -41,9 +43,19 @@ constexpr int kU = 2;          // token loads per wave per pipeline stage
 constexpr int kElems = 16;     // elements of a row held by one lane
 constexpr float kSlack = 8.f;  // log2 units a running max may lag before rescaling
 
+// Cache element types: float, uint16_t (bf16) and uint8_t (FP8 E4M3 codes).
+// Queries and outputs are fp32 with an fp32 cache and bf16 otherwise.
 template <typename T> struct Elem;
-template <> struct Elem<float> { static constexpr int kVecs = 4; };     // 16 floats = 4 x 16 B
-template <> struct Elem<uint16_t> { static constexpr int kVecs = 2; };  // 16 bf16  = 2 x 16 B
+template <> struct Elem<float> { static constexpr int kVecs = 4, kQVecs = 4; };     // 16 floats = 4 x 16 B
+template <> struct Elem<uint16_t> { static constexpr int kVecs = 2, kQVecs = 2; };  // 16 bf16  = 2 x 16 B
+template <> struct Elem<uint8_t> { static constexpr int kVecs = 1, kQVecs = 2; };   // 16 codes = 16 B (q: bf16)
+
+// Two E4M3 codes (the low or the high half of w) as two bf16, exactly (a code
+// has 3 mantissa bits and an exponent well inside bf16's range).
+template <bool HIGH>
+__device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+}
 
 // Partial dot product of a lane's 16 elements of q and k.
 __device__ __forceinline__ float dot16(const u32x4_t* q, const u32x4_t* k, float) {
@@ -61,6 +73,19 @@ __device__ __forceinline__ float dot16(const u32x4_t* q, const u32x4_t* k, uint1
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[j][t]), as_bf16x2(k[j][t]), acc, false);
+  return acc;
+}
+
+// q (16 bf16: elements 2t, 2t+1 in dword t) . k (16 E4M3 codes, 4 per dword)
+__device__ __forceinline__ float dot16(const u32x4_t* q, const u32x4_t* k, uint8_t) {
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[(2 * t) / 4][(2 * t) % 4]), fp8x2_to_bf16x2<false>(k[0][t]),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[(2 * t + 1) / 4][(2 * t + 1) % 4]),
+                                          fp8x2_to_bf16x2<true>(k[0][t]), acc, false);
+  }
   return acc;
 }
 
@@ -139,6 +164,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   constexpr int G = D / kElems;         // lanes per token row
   constexpr int TPW = 64 / G;           // tokens per wave per load
   constexpr int NV = Elem<T>::kVecs;    // 16-byte vectors per lane per row
+  constexpr int QV = Elem<T>::kQVecs;   // 16-byte vectors of a query per lane
+  using TQ = typename std::conditional<sizeof(T) == 4, float, uint16_t>::type;  // query / output type
   constexpr int TOK_IT = TPW * kU;      // tokens per wave per iteration
 
   __shared__ float red_o[kWaves][QH][D];
@@ -166,16 +193,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int grp = lane / G;
   const int sub = lane % G;
-  const float c = a.scale * kLog2e;
+  const float c = a.scale * a.k_scale * kLog2e;
 
-  // this lane's 16 elements of each query head
-  u32x4_t q[QH][NV];
+  // this lane's 16 elements of each query head (the elements of the cache
+  // vectors it loads: interleaved vectors for fp32/bf16, 16 consecutive
+  // elements for FP8)
+  u32x4_t q[QH][QV];
   {
-    const u32x4_t* qv = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + h0) * D);
+    const u32x4_t* qv = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const TQ*>(a.q) + ((size_t)b * a.Hq + h0) * D);
 #pragma unroll
     for (int r = 0; r < QH; ++r)
 #pragma unroll
-      for (int j = 0; j < NV; ++j) q[r][j] = qv[r * (D * sizeof(T) / 16) + j * G + sub];
+      for (int j = 0; j < QV; ++j)
+        q[r][j] = qv[r * (D * sizeof(TQ) / 16) + (sizeof(T) == 1 ? sub * QV + j : j * G + sub)];
   }
 
   float m[QH], l[QH], o[QH][kElems];
@@ -233,7 +263,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
     }
   };
   auto compute = [&](const Buf& B, int t0) {
-    // bf16: element i of the two tokens of this stage, paired for v_dot2
+    // bf16 / FP8: element i of the two tokens of this stage, paired for v_dot2
+    // (token 0 in the low half)
     uint32_t vpair[kElems];
     if constexpr (sizeof(T) == 2) {
       static_assert(kU == 2, "v_dot2 pairs the two token loads of a stage");
@@ -244,6 +275,18 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
           vpair[j * 8 + 2 * t] = __builtin_amdgcn_perm(B.v[1][j][t], B.v[0][j][t], 0x05040100u);
           vpair[j * 8 + 2 * t + 1] = __builtin_amdgcn_perm(B.v[1][j][t], B.v[0][j][t], 0x07060302u);
         }
+    } else if constexpr (sizeof(T) == 1) {
+      static_assert(kU == 2, "v_dot2 pairs the two token loads of a stage");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // bytes (tok0[4t], tok1[4t], tok0[4t+1], tok1[4t+1]) and the next two
+        const uint32_t lo = __builtin_amdgcn_perm(B.v[1][0][t], B.v[0][0][t], 0x05010400u);
+        const uint32_t hi = __builtin_amdgcn_perm(B.v[1][0][t], B.v[0][0][t], 0x07030602u);
+        vpair[4 * t] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(lo));
+        vpair[4 * t + 1] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(lo));
+        vpair[4 * t + 2] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(hi));
+        vpair[4 * t + 3] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(hi));
+      }
     }
 #pragma unroll
     for (int r = 0; r < QH; ++r) {
@@ -274,7 +317,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
         psum += sc[u];
       }
       l[r] += psum;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (sizeof(T) <= 2) {
         // o += p0 V0 + p1 V1 for all 16 elements with one v_dot2 each
         const bf16x2_t pw = as_bf16x2(pack_bf16x2(sc[0], sc[1]));
 #pragma unroll
@@ -347,7 +390,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) combine<1>(mm, ll, &oo, red_ml[w][r][0], red_ml[w][r][1], &red_o[w][r][e]);
     const int h = h0 + r;
-    float out = ll > 0.f ? oo / ll : 0.f;
+    float out = ll > 0.f ? oo / ll * a.v_scale : 0.f;
     float lse = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
     if (any_bad) out = lse = NAN;
     if (ns == 1) {
@@ -418,9 +461,12 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t st) {
-  if (bf16) return a.d == 64 ? launch_d<uint16_t, 64>(a, st) : launch_d<uint16_t, 128>(a, st);
-  return a.d == 64 ? launch_d<float, 64>(a, st) : launch_d<float, 128>(a, st);
+hipError_t launch_decode(const DecodeArgs& a, KvType t, hipStream_t st) {
+  switch (t) {
+    case KvType::BF16: return a.d == 64 ? launch_d<uint16_t, 64>(a, st) : launch_d<uint16_t, 128>(a, st);
+    case KvType::FP8: return a.d == 64 ? launch_d<uint8_t, 64>(a, st) : launch_d<uint8_t, 128>(a, st);
+    default: return a.d == 64 ? launch_d<float, 64>(a, st) : launch_d<float, 128>(a, st);
+  }
 }
 
 }  // namespace fa

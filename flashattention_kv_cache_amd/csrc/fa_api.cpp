@@ -109,7 +109,7 @@ int max_splits_for(int max_seq_len, int split_tokens) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 3; }
+int fa_abi_version(void) { return 4; }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
@@ -246,17 +246,23 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len,
   return o_bytes + l_bytes;
 }
 
-int fa_decode(const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* seq_lens, const int32_t* block_table,
-              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
-              void* o, float* lse,
-              int B, int Hq, int Hkv, int d, float scale, int dtype,
-              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_decode and fa_decode_fp8 share everything but the cache element type.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, const int32_t* block_table,
+                int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
+                void* o, float* lse,
+                int B, int Hq, int Hkv, int d, float scale, fa::KvType kv, float k_scale, float v_scale,
+                int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   int st0 = check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens);
   if (st0 != FA_OK) return st0;
   if (check_window(window, 1) != FA_OK) return FA_ERR_INVALID;
-  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
+  if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
+    return fail(FA_ERR_INVALID, "k_scale and v_scale must be finite and > 0");
   const bool paged = block_table != nullptr;
   if (paged) {
     if (!is_pow2(block_size) || block_size > 1024)
@@ -298,6 +304,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.kv_capacity = kv_capacity; a.max_seq_len = max_seq_len; a.window = window;
   a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = scale;
+  a.k_scale = k_scale; a.v_scale = v_scale;
   a.split_tokens = stoks; a.max_splits = ns;
   if (ns > 1) {
     const size_t slots = (size_t)B * Hq * ns;
@@ -305,7 +312,68 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
     a.ws_o = reinterpret_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
   }
-  hipError_t e = fa::launch_decode(a, dtype == FA_BF16, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_decode(a, kv, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* seq_lens, const int32_t* block_table,
+              int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
+              void* o, float* lse,
+              int B, int Hq, int Hkv, int d, float scale, int dtype,
+              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  return decode_impl(q, k_cache, v_cache, seq_lens, block_table, block_size, max_blocks_per_seq, kv_capacity,
+                     max_seq_len, window, o, lse, B, Hq, Hkv, d, scale,
+                     dtype == FA_BF16 ? fa::KvType::BF16 : fa::KvType::F32, 1.f, 1.f,
+                     split_tokens, workspace, workspace_bytes, stream);
+}
+
+int fa_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* seq_lens, const int32_t* block_table,
+                  int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
+                  void* o, float* lse,
+                  int B, int Hq, int Hkv, int d, float scale, float k_scale, float v_scale,
+                  int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, block_table, block_size, max_blocks_per_seq, kv_capacity,
+                     max_seq_len, window, o, lse, B, Hq, Hkv, d, scale, fa::KvType::FP8, k_scale, v_scale,
+                     split_tokens, workspace, workspace_bytes, stream);
+}
+
+int fa_kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* seq_lens, const int32_t* block_table,
+                     int block_size, int max_blocks_per_seq, int kv_capacity,
+                     int B, int Hkv, int n_new, int d, float k_scale, float v_scale, void* stream) {
+  if (B < 0 || Hkv < 1 || n_new < 0 || d < 1)
+    return fail(FA_ERR_INVALID, "B=%d Hkv=%d n_new=%d d=%d: need B, n_new >= 0 and Hkv, d >= 1", B, Hkv, n_new, d);
+  if (d % 16) return fail(FA_ERR_UNSUPPORTED, "d=%d: an FP8 row must be a multiple of 16 codes", d);
+  if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
+    return fail(FA_ERR_INVALID, "k_scale and v_scale must be finite and > 0");
+  int st0 = check_cache_layout(block_table, block_size, max_blocks_per_seq, kv_capacity, 0);
+  if (st0 != FA_OK) return st0;
+  if (B == 0 || n_new == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(FA_ERR_INVALID, "seq_lens must be 4-byte aligned");
+  if ((long long)B * Hkv > 65535) return fail(FA_ERR_UNSUPPORTED, "B * Hkv must be <= 65535");
+  if ((long long)n_new * (d / 16) > 0x7fffffffll) return fail(FA_ERR_UNSUPPORTED, "n_new too large");
+
+  fa::AppendArgs a{};
+  a.k_new = k_new; a.v_new = v_new; a.k = k_cache; a.v = v_cache;
+  a.seq_lens = seq_lens; a.block_table = block_table;
+  a.block_size = block_table ? block_size : 0;
+  a.log2_block_size = block_table ? ilog2(block_size) : 0;
+  a.max_blocks_per_seq = block_table ? max_blocks_per_seq : 0;
+  a.kv_capacity = kv_capacity;
+  a.B = B; a.Hkv = Hkv; a.n_new = n_new; a.row_chunks = d / 16;
+  a.quantize = 1; a.k_scale = k_scale; a.v_scale = v_scale;
+  hipError_t e = fa::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

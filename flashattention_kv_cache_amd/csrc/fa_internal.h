@@ -39,7 +39,9 @@ struct AppendArgs {
   const int32_t* seq_lens;     // (B) lengths after the append
   const int32_t* block_table;  // nullptr: contiguous
   int block_size, log2_block_size, max_blocks_per_seq, kv_capacity;
-  int B, Hkv, n_new, row_chunks;  // row_chunks: 16-byte chunks per (token, head) row
+  int B, Hkv, n_new, row_chunks;  // row_chunks: 16-byte chunks per (token, head) row of the cache
+  int quantize;                   // 1: bf16 rows into an FP8 (E4M3) cache, code = RNE(x / scale)
+  float k_scale, v_scale;
 };
 
 struct DecodeArgs {
@@ -55,6 +57,7 @@ struct DecodeArgs {
   float* lse;
   int B, Hq, Hkv, d;
   float scale;
+  float k_scale, v_scale;  // FP8 caches: a code stands for value(code) * scale (1 otherwise)
   int split_tokens;   // tokens per split (multiple of 256)
   int max_splits;     // ceil(max_seq_len / split_tokens), >= 1
   float* ws_o;        // (B, Hq, max_splits, d) partial outputs, when max_splits > 1
@@ -63,7 +66,8 @@ struct DecodeArgs {
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
+enum class KvType { F32, BF16, FP8 };  // cache element type (queries/outputs: fp32, bf16, bf16)
+hipError_t launch_decode(const DecodeArgs& a, KvType t, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------

@@ -167,6 +167,32 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_fp8 — fa_decode against a cache of FP8 codes: one byte per cached
+ * number instead of two, so a decode step reads half the bytes.
+ *
+ * Defined by: fa_decode's passages, plus "Генерация и KV-кэш", section
+ * "Сколько весит KV-кэш" (bytes per number: 2 in BF16, 1 in FP8; an FP8 cache
+ * is one of the levers on the cache size).  The pages fix nothing more; the
+ * library's reading: codes are OCP FP8 E4M3 (bias 7, largest magnitude 448,
+ * S.1111.111 = NaN, no infinity) and one fp32 scale per tensor maps a code to
+ * the number value(code) * k_scale (keys) or value(code) * v_scale (values).
+ *
+ *   q, o         (B, Hq, d) bf16
+ *   k_cache,     as fa_decode, elements are E4M3 codes (1 byte)
+ *   v_cache
+ *   k_scale,     finite, > 0
+ *   v_scale
+ *   everything else as fa_decode (the workspace size is the same:
+ *   fa_decode_workspace_bytes)
+ */
+int fa_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* seq_lens, const int32_t* block_table,
+                  int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
+                  void* o, float* lse,
+                  int B, int Hq, int Hkv, int d, float scale, float k_scale, float v_scale,
+                  int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_kv_append — write the keys and values of n_new new tokens per sequence
  * into a KV cache, at positions L_b - n_new .. L_b - 1 of sequence b (L_b =
  * seq_lens[b], the length AFTER the append).  A pure copy: the cache receives
@@ -197,6 +223,24 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
                  const int32_t* seq_lens, const int32_t* block_table,
                  int block_size, int max_blocks_per_seq, int kv_capacity,
                  int B, int Hkv, int n_new, int d, int dtype, void* stream);
+
+/*
+ * fa_kv_append_fp8 — fa_kv_append into an FP8 (E4M3) cache: each bf16 value x
+ * of the new rows is stored as the code of x / scale (k_scale for keys,
+ * v_scale for values), the quotient formed in fp32 (IEEE division), saturated
+ * to +-448 and rounded to the nearest code, ties to the even code; a NaN stays
+ * NaN.  The scale convention is the one fa_decode_fp8 reads back.
+ *
+ *   k_new, v_new (B, Hkv, n_new, d) bf16
+ *   k_cache,     (B, Hkv, kv_capacity, d) or (kv_capacity, block_size, Hkv, d)
+ *   v_cache      E4M3 codes
+ *
+ * Contract: as fa_kv_append, with d a multiple of 16 and finite scales > 0.
+ */
+int fa_kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* seq_lens, const int32_t* block_table,
+                     int block_size, int max_blocks_per_seq, int kv_capacity,
+                     int B, int Hkv, int n_new, int d, float k_scale, float v_scale, void* stream);
 
 /*
  * fa_chunked_prefill — attention of the Nq newest tokens of each sequence

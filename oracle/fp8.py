@@ -77,13 +77,26 @@ def quantize_e4m3(x, scale: float) -> np.ndarray:
     return out
 
 
+class _Decoded:
+    """A cache of codes seen as the numbers they stand for, decoded on access
+    (value(code) * scale), so that a multi-GiB cache is never expanded whole."""
+
+    def __init__(self, codes, scale: float):
+        self.codes = _codes(codes)
+        self.scale = float(scale)
+        self.shape = self.codes.shape
+
+    def __getitem__(self, idx):
+        return decode_codes(self.codes[idx]) * self.scale
+
+
 def decode_fp8(q, k_codes, v_codes, seq_lens, scale: float, k_scale: float, v_scale: float,
                block_table=None, block_size: int = 0, heads=None, window: int = 0):
     """Decode against an FP8 cache: the caches hold E4M3 codes (contiguous
     (B, Hkv, S_cap, d) or a paged pool (num_blocks, block_size, Hkv, d)); their
     values are decode(code) * k_scale and decode(code) * v_scale."""
-    K = decode_codes(k_codes) * k_scale
-    V = decode_codes(v_codes) * v_scale
+    K = _Decoded(k_codes, k_scale)
+    V = _Decoded(v_codes, v_scale)
     if block_table is None:
         return decode_contiguous(q, K, V, seq_lens, scale, heads=heads, window=window)
     return decode_paged(q, K, V, block_table, seq_lens, block_size, scale, heads=heads, window=window)

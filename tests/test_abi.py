@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_abi_version", "fa_decode_split_tokens", "fa_kv_append",
-                 "fa_chunked_prefill"):
+                 "fa_chunked_prefill", "fa_decode_fp8", "fa_kv_append_fp8"):
         assert want in names
 
 
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(fa):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(fa.SIGNATURES) == set(declared_functions())
-    assert L.fa_abi_version() == 3
+    assert L.fa_abi_version() == 4
 
 
 def test_status_strings(fa):
@@ -226,6 +226,58 @@ def test_kv_append_empty_is_a_noop(fa):
     assert append(fa, kn=0, vn=0, k=0, v=0, lens=0, n=0, d=8, dtype=F32) == FA_OK
 
 
+def decode_fp8(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, window=0, o=A, lse=A,
+               B=2, Hq=8, Hkv=2, d=128, scale=0.1, ks=0.5, vs=0.5, split=0, ws=None, ws_bytes=0):
+    P = ctypes.c_void_p
+    return fa.lib().fa_decode_fp8(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, window, P(o), P(lse),
+                                  B, Hq, Hkv, d, scale, ks, vs, split, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), FA_ERR_INVALID, "divide"),
+    (dict(d=96), FA_ERR_UNSUPPORTED, "head dim"),
+    (dict(ks=0.0), FA_ERR_INVALID, "k_scale"),
+    (dict(vs=float("inf")), FA_ERR_INVALID, "v_scale"),
+    (dict(ks=float("nan")), FA_ERR_INVALID, "k_scale"),
+    (dict(scale=-1.0), FA_ERR_INVALID, "scale"),
+    (dict(window=-1), FA_ERR_INVALID, "window"),
+    (dict(table=A, bs=6), FA_ERR_INVALID, "power of two"),
+    (dict(q=0), FA_ERR_INVALID, "null"),
+    (dict(v=MIS), FA_ERR_INVALID, "aligned"),
+    (dict(maxlen=1024, cap=1024, split=256), FA_ERR_INVALID, "workspace"),
+])
+def test_decode_fp8_rejects(fa, kw, status, msg):
+    assert decode_fp8(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def append_fp8(fa, kn=A, vn=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, B=2, Hkv=2, n=4, d=128,
+               ks=1.0, vs=1.0):
+    P = ctypes.c_void_p
+    return fa.lib().fa_kv_append_fp8(P(kn), P(vn), P(k), P(v), P(lens), P(table), bs, mbps, cap, B, Hkv, n, d,
+                                     ks, vs, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(B=-1), FA_ERR_INVALID, "B=-1"),
+    (dict(d=40), FA_ERR_UNSUPPORTED, "multiple of 16"),
+    (dict(ks=-2.0), FA_ERR_INVALID, "k_scale"),
+    (dict(vs=0.0), FA_ERR_INVALID, "v_scale"),
+    (dict(table=A, bs=5), FA_ERR_INVALID, "power of two"),
+    (dict(k=0), FA_ERR_INVALID, "null"),
+    (dict(kn=MIS), FA_ERR_INVALID, "aligned"),
+    (dict(B=70000, Hkv=1), FA_ERR_UNSUPPORTED, "65535"),
+])
+def test_kv_append_fp8_rejects(fa, kw, status, msg):
+    assert append_fp8(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_fp8_empty_calls_are_noops(fa):
+    assert decode_fp8(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, B=0) == FA_OK
+    assert append_fp8(fa, kn=0, vn=0, k=0, v=0, lens=0, n=0) == FA_OK
+
+
 def test_no_cpu_fallback_without_gpu(fa):
     """On a machine without a GPU the binding raises instead of computing."""
     import torch
@@ -239,3 +291,6 @@ def test_no_cpu_fallback_without_gpu(fa):
         fa.chunked_prefill(q, q, q, lens)
     with pytest.raises(ValueError, match="GPU tensor"):
         fa.kv_append(q, q, q, q, lens)
+    qb = torch.zeros(1, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.decode_fp8(qb, q.to(torch.uint8), q.to(torch.uint8), lens, 1.0, 1.0)
