@@ -17,7 +17,7 @@ plus q, o, lse and the block-table entries read).  Kernel durations come from
 HIP events recorded around each launch on the stream the kernels run on.
 ``extras`` (outside the step, skipped with --no-extras) times the KV append,
 the chunked prefill against a paged cache, sliding-window prefill and decode,
-and decode against an FP8 cache, each on its own.
+decode against an FP8 cache and MLA decode, each on its own.
 """
 from __future__ import annotations
 
@@ -216,6 +216,33 @@ def extras(dev, steps: int, dec):
                                       "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                       "kernel": "decode_split_kernel<fp8,128,4,paged> + decode_merge_kernel"}}
     del fk, fv
+
+    # MLA decode (absorbed latent form), DeepSeek-V3-shaped batch
+    wm = W.MLA_DECODE
+    mi = W.mla_inputs(wm)
+    mq, mkv = mi.q.to(dev), mi.kv.to(dev)
+    ml, mt = mi.seq_lens.to(dev), mi.block_table.to(dev)
+    mo = torch.empty((wm.B, wm.Hq, wm.d_c), dtype=torch.bfloat16, device=dev)
+    mlse = torch.empty((wm.B, wm.Hq), dtype=torch.float32, device=dev)
+    st = binding.mla_decode_split_tokens(wm.B, wm.Hq, mi.max_seq_len)
+    ws = torch.empty(max(1, binding.mla_decode_workspace_bytes(wm.B, wm.Hq, mi.max_seq_len, st)),
+                     dtype=torch.uint8, device=dev)
+    m_avg, m_med = time_launches(lambda: binding.mla_decode(mq, mkv, ml, wm.scale, block_table=mt,
+                                                            max_seq_len=mi.max_seq_len, split_tokens=st,
+                                                            workspace=ws, out=mo, lse=mlse), steps, 20)
+    mflops = wm.flops(mi.seq_lens.tolist())
+    mbytes = mi.kv_bytes() + mq.numel() * 2 + mo.numel() * 2 + mlse.numel() * 4 + \
+        int(((mi.seq_lens.to(torch.int64) + wm.block_size - 1) // wm.block_size).sum()) * 4 + wm.B * 4
+    tf = mflops / (m_avg * 1e-3) / 1e12
+    gbs = mbytes / (m_avg * 1e-3) / 1e9
+    out["mla_decode"] = {"workload": wm.name, "value": round(tf, 3), "unit": "TFLOP/s", "kernel_ms": round(m_avg, 5),
+                         "kernel_ms_median": round(m_med, 5), "flops": mflops, "bytes": mbytes, "split_tokens": st,
+                         "hbm_GBps": round(gbs, 2),
+                         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                      "kernel": "mla_split_kernel + mla_merge_kernel",
+                                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del mq, mkv, mo
     return out
 
 

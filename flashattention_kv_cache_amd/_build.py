@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "kv_append.hip"]
+SOURCES = ["fa_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "kv_append.hip", "mla_decode.hip"]
 ARCH = "gfx950"
 
 

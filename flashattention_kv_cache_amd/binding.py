@@ -32,6 +32,9 @@ SIGNATURES = {
     "fa_chunked_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "fa_decode_fp8": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _F, _F, _I, _P, _S, _P], _I),
     "fa_kv_append_fp8": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P], _I),
+    "fa_mla_decode": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P], _I),
+    "fa_mla_decode_split_tokens": ([_I, _I, _I, _I, _I], _I),
+    "fa_mla_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _S),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -298,4 +301,59 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
                            _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
                            int(split_tokens), _ptr(workspace) if need else None, ws_bytes,
                            _stream(stream)))
+    return out, lse
+
+
+MLA_DC, MLA_DR = 512, 64
+
+
+def mla_decode_split_tokens(B: int, Hq: int, max_seq_len: int) -> int:
+    return int(lib().fa_mla_decode_split_tokens(B, Hq, MLA_DC, MLA_DR, max_seq_len))
+
+
+def mla_decode_workspace_bytes(B: int, Hq: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    return int(lib().fa_mla_decode_workspace_bytes(B, Hq, MLA_DC, MLA_DR, max_seq_len, split_tokens))
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+               block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None,
+               split_tokens: int = 0, workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fa_mla_decode: bf16 q (B, Hq, 576) = [absorbed latent query ; position
+    query] against cache rows [latent (512) ; position key (64)], contiguous
+    (B, S_cap, 576) or a paged pool (num_blocks, block_size, 576) with
+    ``block_table``.  Returns the latent-space output (B, Hq, 512) and LSE."""
+    for t, n in ((q, "q"), (kv_cache, "kv_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    if q.dtype != torch.bfloat16 or kv_cache.dtype != torch.bfloat16:
+        raise TypeError("fa_mla_decode takes bf16 queries and cache")
+    if q.dim() != 3 or kv_cache.dim() != 3 or q.shape[2] != MLA_DC + MLA_DR or kv_cache.shape[2] != q.shape[2]:
+        raise ValueError("expected q (B, Hq, 576) and a cache of 576-wide rows")
+    B, Hq, _ = q.shape
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 with one entry per sequence")
+    if block_table is not None:
+        _dev(block_table, "block_table")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 (B, max_blocks)")
+        nblk, bs, _ = kv_cache.shape
+        capacity, max_blocks, bound = nblk, block_table.shape[1], block_table.shape[1] * bs
+    else:
+        if kv_cache.shape[0] != B:
+            raise ValueError("cache batch != q batch")
+        bs, capacity, max_blocks, bound = 0, kv_cache.shape[1], 0, kv_cache.shape[1]
+    if max_seq_len is None:
+        max_seq_len = bound
+    need = mla_decode_workspace_bytes(B, Hq, max_seq_len, split_tokens)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, MLA_DC), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_mla_decode(_ptr(q), _ptr(kv_cache), _ptr(seq_lens), _ptr(block_table), bs, max_blocks, capacity,
+                               int(max_seq_len), _ptr(out), _ptr(lse), B, Hq, MLA_DC, MLA_DR, float(scale),
+                               int(split_tokens), _ptr(workspace) if need else None, ws_bytes, _stream(stream)))
     return out, lse

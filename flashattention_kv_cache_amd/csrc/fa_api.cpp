@@ -101,6 +101,29 @@ int decode_span(int max_seq_len, int window) {
   return window > 0 && window < max_seq_len ? window : max_seq_len;
 }
 
+// MLA decode: a split writes 512 fp32 per head (256 KiB for 128 heads), so
+// splits are long: about two workgroups per CU if every sequence had
+// max_seq_len tokens, and never under 1024 tokens.  Multiples of 256.
+int choose_mla_split_tokens(int B, int Hq, int max_seq_len) {
+  const double groups = (double)B * ((Hq + 127) / 128);
+  long long st = (long long)(groups * max_seq_len / 512.0);
+  st = (st + 255) / 256 * 256;
+  if (st < 1024) st = 1024;
+  if (st > 16384) st = 16384;
+  return (int)st;
+}
+
+int check_mla_sizes(int B, int Hq, int d_c, int d_r, int max_seq_len, int split_tokens) {
+  if (B < 0 || Hq < 1 || max_seq_len < 0)
+    return fail(FA_ERR_INVALID, "B=%d Hq=%d max_seq_len=%d: need B >= 0, Hq >= 1, max_seq_len >= 0", B, Hq,
+                max_seq_len);
+  if (d_c != 512 || d_r != 64)
+    return fail(FA_ERR_UNSUPPORTED, "latent width %d + position key %d not built (512 + 64)", d_c, d_r);
+  if (split_tokens < 0 || split_tokens % 32)
+    return fail(FA_ERR_INVALID, "split_tokens %d must be 0 or a positive multiple of 32", split_tokens);
+  return FA_OK;
+}
+
 int max_splits_for(int max_seq_len, int split_tokens) {
   return max_seq_len <= split_tokens ? 1 : (max_seq_len + split_tokens - 1) / split_tokens;
 }
@@ -109,7 +132,7 @@ int max_splits_for(int max_seq_len, int split_tokens) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 4; }
+int fa_abi_version(void) { return 5; }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
@@ -343,6 +366,67 @@ int fa_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
   return decode_impl(q, k_cache, v_cache, seq_lens, block_table, block_size, max_blocks_per_seq, kv_capacity,
                      max_seq_len, window, o, lse, B, Hq, Hkv, d, scale, fa::KvType::FP8, k_scale, v_scale,
                      split_tokens, workspace, workspace_bytes, stream);
+}
+
+int fa_mla_decode_split_tokens(int B, int Hq, int d_c, int d_r, int max_seq_len) {
+  if (check_mla_sizes(B, Hq, d_c, d_r, max_seq_len, 0) != FA_OK) return 0;
+  return choose_mla_split_tokens(B, Hq, max_seq_len);
+}
+
+size_t fa_mla_decode_workspace_bytes(int B, int Hq, int d_c, int d_r, int max_seq_len, int split_tokens) {
+  if (check_mla_sizes(B, Hq, d_c, d_r, max_seq_len, split_tokens) != FA_OK) return 0;
+  const int st = split_tokens ? split_tokens : choose_mla_split_tokens(B, Hq, max_seq_len);
+  const int ns = max_splits_for(max_seq_len, st);
+  if (ns <= 1) return 0;
+  const size_t slots = (size_t)B * Hq * ns;
+  const size_t o_bytes = (slots * d_c * sizeof(float) + 255) & ~(size_t)255;
+  const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
+  return o_bytes + l_bytes;
+}
+
+int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, const int32_t* block_table,
+                  int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+                  void* o, float* lse, int B, int Hq, int d_c, int d_r, float scale,
+                  int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  int st0 = check_mla_sizes(B, Hq, d_c, d_r, max_seq_len, split_tokens);
+  if (st0 != FA_OK) return st0;
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite and > 0");
+  st0 = check_cache_layout(block_table, block_size, max_blocks_per_seq, kv_capacity, max_seq_len);
+  if (st0 != FA_OK) return st0;
+  if (B == 0) return ok();
+  if (!q || !kv_cache || !seq_lens || !o) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(FA_ERR_INVALID, "seq_lens must be 4-byte aligned");
+  const int stoks = split_tokens ? split_tokens : choose_mla_split_tokens(B, Hq, max_seq_len);
+  const int ns = max_splits_for(max_seq_len, stoks);
+  const size_t need = fa_mla_decode_workspace_bytes(B, Hq, d_c, d_r, max_seq_len, split_tokens);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_INVALID, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
+  if (B > 65535 || ns > 0x7fffffff || (Hq + 127) / 128 > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (B <= 65535)");
+
+  fa::MlaArgs a{};
+  a.q = q; a.kv = kv_cache; a.seq_lens = seq_lens; a.block_table = block_table;
+  a.block_size = block_table ? block_size : 0;
+  a.log2_block_size = block_table ? ilog2(block_size) : 0;
+  a.max_blocks_per_seq = block_table ? max_blocks_per_seq : 0;
+  a.kv_capacity = kv_capacity; a.max_seq_len = max_seq_len;
+  a.o = o; a.lse = lse; a.B = B; a.Hq = Hq; a.scale = scale;
+  a.split_tokens = stoks; a.max_splits = ns;
+  if (ns > 1) {
+    const size_t slots = (size_t)B * Hq * ns;
+    const size_t o_bytes = (slots * d_c * sizeof(float) + 255) & ~(size_t)255;
+    a.ws_o = reinterpret_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+  }
+  hipError_t e = fa::launch_mla_decode(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int fa_kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

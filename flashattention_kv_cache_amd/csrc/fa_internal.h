@@ -66,6 +66,23 @@ struct DecodeArgs {
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+struct MlaArgs {
+  const void* q;               // (B, Hq, DC + DR) bf16: [absorbed content query ; position query]
+  const void* kv;              // rows [latent ; position key]: contiguous (B, kv_capacity, DC + DR) or
+                               // a pool (kv_capacity blocks, block_size, DC + DR), bf16
+  const int32_t* seq_lens;
+  const int32_t* block_table;  // nullptr: contiguous
+  int block_size, log2_block_size, max_blocks_per_seq, kv_capacity, max_seq_len;
+  void* o;                     // (B, Hq, DC) bf16
+  float* lse;                  // (B, Hq) or nullptr
+  int B, Hq;
+  float scale;
+  int split_tokens, max_splits;
+  float* ws_o;                 // (B, Hq, max_splits, DC) partial outputs, when max_splits > 1
+  float* ws_lse;               // (B, Hq, max_splits)
+};
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
+
 enum class KvType { F32, BF16, FP8 };  // cache element type (queries/outputs: fp32, bf16, bf16)
 hipError_t launch_decode(const DecodeArgs& a, KvType t, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
@@ -135,5 +152,42 @@ __device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------
+// LDS tiles of the MFMA kernels.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// Forces a value to be computed at this point of the program (an empty asm
+// that reads it; no instruction is emitted).  Used so that the softmax of a
+// tile is not sunk past the barrier into the next stage, where it could no
+// longer overlap this stage's MFMAs.
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(const u32x4_t& x) { asm volatile("" ::"v"(x)); }
+
+// Direct global -> LDS copies (global_load_lds_dwordx4).  A wave instruction
+// writes 1 KiB of consecutive LDS starting at M0 (lane L at 16 L); lane L
+// fetches the global chunk that the kernel's swizzle places there.
+//
+// They are issued from inline assembly on purpose: the compiler cannot tell
+// which LDS bytes such a load writes, and would otherwise drain every one of
+// them (s_waitcnt vmcnt(0)) before the next transposed LDS read, i.e. in the
+// middle of the tile that overlaps them.  The instruction writes no VGPR, so
+// no register can be reused under it; the kernel itself waits for all of
+// them (wait_all_vmem) before the barrier that publishes the tile, and
+// vector-memory loads retire in order, so the compiler's own waits for other
+// loads stay correct (only stricter).  M0 is written in the same block and
+// declared clobbered; s_nop 0 covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma_saddr(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_vaddr(const void* vaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(vaddr), "s"(lds_addr) : "memory", "m0");
+}
+
 
 }  // namespace fa

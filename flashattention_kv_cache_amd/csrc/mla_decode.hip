@@ -1,0 +1,340 @@
+// Multi-head latent attention (MLA) decode on the gfx950 matrix cores.
+//
+// What is computed ("Module 09: Efficient Attention", sections "The Math:
+// Compress, Reconstruct, Decouple" and "Why RoPE Has To Be Decoupled"): the
+// cache holds, per token, one row [c ; k^R] — the latent (DC = 512 numbers)
+// and the decoupled position key (DR = 64) — shared by every head.  With the
+// content query absorbed into latent space (q^lat_h = W^UK_h^T q^C_h, done by
+// the caller), head h scores token j as [q^lat_h ; q^R_h] . [c_j ; k^R_j]
+// times `scale` (the page: 1 / sqrt(d_head + d_r)), and its output is the
+// softmax-weighted sum of the latents c_j, in latent space (the caller applies
+// W^UV_h afterwards).  So every head attends one shared key of width 576 and
+// one shared value of width 512 — the first 512 numbers of the same row.
+//
+// With 128 heads per token this is a dense contraction (4 flop per head per
+// cached number, ~128 flop per cached byte), so it runs on MFMA
+// (v_mfma_f32_16x16x32_bf16):
+//   * a workgroup (8 waves, two per SIMD) takes 128 heads of one sequence and
+//     one split of its tokens; wave w owns heads 16w .. 16w + 15.  Q^T
+//     (576 x 16) of a wave stays in registers as the B operand of S^T = K Q^T
+//     (2 key blocks x 18 k-steps per 32-key tile); O^T (512 x 16, fp32, 128
+//     registers) accumulates O^T += V^T P^T (32 dim blocks, one k-step of all
+//     32 keys).  Sixteen heads per wave keep the wave within 256 registers;
+//     32 would need 256 accumulators alone;
+//   * 32-key tiles of cache rows go HBM -> LDS with global_load_lds_dwordx4,
+//     double buffered; one tile serves both products (V is a prefix of K);
+//   * rows are 72 sixteen-byte units; unit u of row r sits at u ^ s(r) with
+//     s(r) the bit-reversed (r >> 1) & 7, which keeps both the K operand reads
+//     (16 rows at one unit) and the transposed V reads (8 rows x 2 units) free
+//     of bank conflicts on the 64-bank LDS;
+//   * the S^T accumulator gives a lane keys 4 g + i and 16 + 4 g + i (g = lane
+//     / 16) of its head: packed in that order they are the B operand of PV as
+//     they stand, and the transposed V reads fetch the same key rows;
+//   * the streaming softmax (running max with a lazy rescale, fp32 row sum of
+//     the unrounded weights, bf16 weights into PV) is the prefill kernel's;
+//   * splits of a sequence write (output, log-sum-exp) partials that a merge
+//     kernel combines with weights exp(lse_s - max lse).
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kDC = 512, kDR = 64, kDK = kDC + kDR;  // latent, position key, key width
+constexpr int kUnits = kDK / 8;                       // 16-byte units per cache row (72)
+constexpr int kBN = 32;                               // keys per tile
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kHeadsWave = 16, kHeadsWG = kHeadsWave * kWaves;  // 16 per wave, 128 per workgroup
+constexpr int kKS = kDK / 32;                         // k-steps of S^T = K Q^T (18)
+constexpr int kDB = kDC / 16;                         // 16-row blocks of O^T (32)
+constexpr int kInstr = kBN * kUnits / 64;             // direct loads per tile (36)
+constexpr float kSlack = 8.f;                         // log2 units a running max may lag
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Physical unit of logical unit u in row r: only the low three bits move.
+__device__ __forceinline__ int swz(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | (x >> 2);
+}
+
+struct Smem {
+  uint16_t kv[2][kBN * kDK];  // 2 x 36 KiB
+};
+
+// Waves issue the 36 direct loads of a tile round-robin: wave w takes loads
+// w, w + 8, ...; waves 0-3 issue 5, waves 4-7 issue 4.  s_waitcnt vmcnt(n),
+// other counters not waited: all but this wave's last n vector-memory
+// operations are done.
+__device__ __forceinline__ void wait_all_but_last_tile(int wave) {
+  if (wave < kInstr % kWaves) __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves + 1));
+  else __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves));
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
+  __shared__ Smem sm;
+  const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, col = lane & 15;
+
+  const int L = a.seq_lens[b];
+  bool bad = L < 0 || L > a.max_seq_len;
+  const int ns = bad ? 1 : max(1, (L + a.split_tokens - 1) / a.split_tokens);
+  if (s >= ns) return;
+  const int t_begin = bad ? 0 : s * a.split_tokens;
+  const int t_end = bad ? 0 : min(L, t_begin + a.split_tokens);
+  const int n_tiles = (t_end - t_begin + kBN - 1) / kBN;
+
+  const int h = hg * kHeadsWG + wave * kHeadsWave + col;  // this lane's head
+  const bool wave_live = hg * kHeadsWG + wave * kHeadsWave < a.Hq;
+
+  // ---- Q^T operand fragments: head h, dims 32 ks + 8 g .. + 7
+  bf16x8_t qf[kKS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + min(h, a.Hq - 1)) * kDK + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 32);
+  }
+  f32x4 oacc[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l0 = 0.f, l1 = 0.f;
+  const float c = a.scale * kLog2e;
+
+  // ---- tile copy.  Load i of a tile fills units 64 i .. 64 i + 63 of the
+  // tile's 32 x 72 units; lane L takes unit u = 64 i + L: row u / 72, physical
+  // unit u % 72, whose logical unit it fetches.  A paged tile lies in one block
+  // when block_size >= 32, and in two (rows 0-15: loads 0-17, rows 16-31: loads
+  // 18-35) when block_size is 16; smaller blocks and the split's last tile
+  // take the per-lane path.
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv);
+  const int32_t* trow = a.block_table ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
+  const int bs = a.block_size, lbs = a.log2_block_size;
+  const bool blocky = trow == nullptr || bs >= 16;
+  auto lds_of = [&](int buf) { return (uint32_t)(uintptr_t)(const lds_u16*)sm.kv[buf]; };
+  auto entry = [&](int tok) { return trow[min(tok, t_end - 1) >> lbs]; };
+  auto copy_tile = [&](int t, int buf, int e0, int e1) {
+    const int tok0 = t_begin + t * kBN;
+    const uint32_t lds0 = lds_of(buf);
+    // The per-lane unit arithmetic below is cheap; recomputing it per tile
+    // (the empty asm hides that it is loop-invariant) keeps ~15 registers free.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (blocky && tok0 + kBN <= t_end) {
+      if (trow) {
+        e0 = __builtin_amdgcn_readfirstlane(e0);
+        e1 = __builtin_amdgcn_readfirstlane(e1);
+        if (e0 < 0 || e0 >= a.kv_capacity) { bad = true; e0 = 0; }
+        if (bs == 16 && (e1 < 0 || e1 >= a.kv_capacity)) { bad = true; e1 = 0; }
+      }
+#pragma unroll
+      for (int k = 0; k < (kInstr + kWaves - 1) / kWaves; ++k) {
+        const int i = wave + kWaves * k;
+        if (i >= kInstr) break;
+        const int u = 64 * i + ln, r = u / kUnits, p = u - r * kUnits;
+        const int lu = p ^ swz(r);
+        const uint16_t* base;
+        int rr = r;
+        if (trow) {
+          const int half = bs == 16 ? i / (kInstr / 2) : 0;  // which block of the tile
+          rr = r - 16 * half;
+          base = kv + ((size_t)(half ? e1 : e0) * bs + ((tok0 + 16 * half) & (bs - 1))) * kDK;
+        } else {
+          base = kv + ((size_t)b * a.kv_capacity + tok0) * kDK;
+        }
+        lds_dma_saddr((uint32_t)((rr * kDK + lu * 8) * 2), base, lds0 + i * 1024);
+      }
+    } else {
+      // each lane finds its own token; rows past the split read its last
+      // token (weight 0, finite)
+#pragma unroll
+      for (int k = 0; k < (kInstr + kWaves - 1) / kWaves; ++k) {
+        const int i = wave + kWaves * k;
+        if (i >= kInstr) break;
+        const int u = 64 * i + ln, r = u / kUnits, p = u - r * kUnits;
+        const int lu = p ^ swz(r);
+        const int tok = min(tok0 + r, t_end - 1);
+        size_t row;
+        if (trow) {
+          int blk = trow[tok >> lbs];
+          if (blk < 0 || blk >= a.kv_capacity) { bad = true; blk = 0; }
+          row = (size_t)blk * bs + (tok & (bs - 1));
+        } else {
+          row = (size_t)b * a.kv_capacity + tok;
+        }
+        lds_dma_vaddr(kv + row * kDK + lu * 8, lds0 + i * 1024);
+      }
+    }
+  };
+
+  // LDS element offsets.  Only the low three bits of a unit index are
+  // swizzled, so every offset is a lane-dependent base plus a constant.
+  //   K operand of key block kb, k-step ks: row 16 kb + col, unit 4 ks + g,
+  //     low bits 4 (ks % 2) + g -> kbase[kb][ks % 2] + 64 (ks / 2);
+  //   V^T operand of dim block db: rows 4 g + j (keys 0-15 half) and
+  //     16 + 4 g + j, dims 16 db + 4 a (j = lane % 16 / 4, a = lane % 4), unit
+  //     2 db + a / 2, low bits 2 (db % 4) + a / 2 -> vbase[db % 4] + 64 (db / 4)
+  //     (+ 16 rows for the second half).
+  int kbase[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      kbase[kb][par] = (16 * kb + col) * kDK + (((4 * par + g) ^ swz(col)) << 3);
+  const int vj = (lane & 15) >> 2, va = lane & 3;
+  const int vrow = 4 * g + vj;
+  int vbase[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vbase[q] = vrow * kDK + (((2 * q + (va >> 1)) ^ swz(vrow)) << 3) + 4 * (va & 1);
+
+  // ---- prologue: tiles 0 and 1
+  int e0 = 0, e1 = 0;
+  const bool look = trow && blocky;
+  if (n_tiles > 0) {
+    copy_tile(0, 0, look ? entry(t_begin) : 0, look ? entry(t_begin + 16) : 0);
+    if (n_tiles > 1) copy_tile(1, 1, look ? entry(t_begin + kBN) : 0, look ? entry(t_begin + kBN + 16) : 0);
+  }
+  wait_all_vmem();
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (look && t + 2 < n_tiles) {  // block ids of tile t + 2, landing during this tile
+      e0 = entry(t_begin + (t + 2) * kBN);
+      e1 = entry(t_begin + (t + 2) * kBN + 16);
+    }
+    if (wave_live) {
+      // S^T = K Q^T: keys 16 kb + 4 g + i of head col in sacc[kb][i]
+      f32x4 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.kv[buf][kbase[kb][ks & 1] + 64 * (ks >> 1)]);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb],
+                                                             0, 0, 0);
+        }
+      if (t == n_tiles - 1) {  // keys past the split get weight 0
+        const int lim = t_end - 1 - (t_begin + t * kBN + 4 * g);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * kb + i > lim) sacc[kb][i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = halves_max(mx) * c;  // the head's max over all 32 keys
+      const float mn = fmaxf(m, mx);
+      if (__any(mn > m + kSlack)) {
+        const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) oacc[i] *= alpha;
+        l0 *= alpha;
+        l1 *= alpha;
+        m = mn;
+      }
+      const float mu = (m == -INFINITY) ? 0.f : m;
+      float p[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[kb][i] = fast_exp2(fmaf(sacc[kb][i], c, -mu));
+          if (kb) l1 += p[kb][i]; else l0 += p[kb][i];
+        }
+      u32x4_t w;
+      w[0] = pack_bf16x2(p[0][0], p[0][1]);
+      w[1] = pack_bf16x2(p[0][2], p[0][3]);
+      w[2] = pack_bf16x2(p[1][0], p[1][1]);
+      w[3] = pack_bf16x2(p[1][2], p[1][3]);
+      const bf16x8_t pc = __builtin_bit_cast(bf16x8_t, w);
+      // O^T += V^T P^T, one k-step of 32 keys per 16-dim block
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int off = vbase[db & 3] + 64 * (db >> 2);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.kv[buf] + off));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.kv[buf] + off + 16 * kDK));
+        const bf16x8_t va8 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va8, pc, oacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with buffer buf
+    if (t + 2 < n_tiles) {
+      copy_tile(t + 2, buf, e0, e1);
+      wait_all_but_last_tile(wave);  // tile t + 1 has landed (this wave's loads)
+    } else {
+      wait_all_vmem();
+    }
+    __syncthreads();  // ... and every wave's
+  }
+
+  // ---- epilogue
+  const bool any_bad = __syncthreads_or(bad);
+  float lt = l0 + l1;
+  lt += __shfl_xor(lt, 16);
+  lt = halves_sum(lt);
+  if (!wave_live || h >= a.Hq) return;
+  const float inv = any_bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = any_bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+  if (ns == 1) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + ((size_t)b * a.Hq + h) * kDC + 4 * g;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      u32x2_t w2;
+      w2[0] = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
+      w2[1] = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
+      *reinterpret_cast<u32x2_t*>(op + 16 * db) = w2;
+    }
+    if (a.lse && g == 0) a.lse[(size_t)b * a.Hq + h] = lse;
+  } else {
+    const size_t slot = ((size_t)b * a.Hq + h) * a.max_splits + s;
+    float* op = a.ws_o + slot * kDC + 4 * g;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = oacc[db] * inv;
+    if (g == 0) a.ws_lse[slot] = lse;
+  }
+}
+
+// One (sequence, head) per workgroup: the splits' outputs weighted by
+// exp(lse_s - max_s lse_s).
+__global__ __launch_bounds__(kDC / 4) void mla_merge_kernel(MlaArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int L = a.seq_lens[b];
+  const bool bad = L < 0 || L > a.max_seq_len;
+  const int ns = bad ? 1 : max(1, (L + a.split_tokens - 1) / a.split_tokens);
+  if (ns == 1) return;  // written by the split kernel
+  const size_t slot0 = (size_t)bh * a.max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[slot0 + s]);
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int e = threadIdx.x * 4;
+  for (int s = 0; s < ns; ++s) {
+    const float w = __expf(a.ws_lse[slot0 + s] - M);
+    wsum += w;
+    acc += w * *reinterpret_cast<const f32x4*>(a.ws_o + (slot0 + s) * kDC + e);
+  }
+  const float inv = 1.f / wsum;
+  u32x2_t out;
+  out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.o) + (size_t)bh * kDC + e) = out;
+  if (a.lse && threadIdx.x == 0) a.lse[bh] = M + __logf(wsum);
+}
+
+}  // namespace
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
+  const int hgroups = (a.Hq + kHeadsWG - 1) / kHeadsWG;
+  dim3 grid(a.max_splits, a.B, hgroups);
+  hipLaunchKernelGGL(mla_split_kernel, grid, dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_splits == 1) return e;
+  hipLaunchKernelGGL(mla_merge_kernel, dim3(a.B * a.Hq), dim3(kDC / 4), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -57,22 +57,11 @@ constexpr int kBN = 64;   // keys per tile
 constexpr int kThreads = 256;
 constexpr float kSlack = 8.f;  // log2 units a running max may lag before rescaling
 
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-
 template <int D>
 struct Smem {
   uint16_t k[2][kBN * D];  // row-major K tiles, chunks swizzled by row % 8
   uint16_t v[2][kBN * D];  // row-major V tiles, chunks swizzled by 2 * (row % 4)
 };
-
-// Forces a value to be computed at this point of the program (an empty asm
-// that reads it; no instruction is emitted).  Used so that the softmax of a
-// tile is not sunk past the barrier into the next stage, where it could no
-// longer overlap this stage's MFMAs.
-__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ void pin(const u32x4_t& x) { asm volatile("" ::"v"(x)); }
 
 // The LDS has 64 banks of 4 bytes: a 16-byte read is served 16 lanes per
 // cycle, an 8-byte read 32 lanes per cycle.  Swizzles are XOR masks on the
@@ -84,28 +73,6 @@ __device__ __forceinline__ void pin(const u32x4_t& x) { asm volatile("" ::"v"(x)
 //     d=128: mask = 4 (row % 4);  d=64: mask = 4 ((row/2) % 2).
 template <int D> __device__ __forceinline__ int k_swz(int row) { return (row / (128 / D)) & (D / 8 - 1); }
 template <int D> __device__ __forceinline__ int v_swz(int row) { return ((row / (128 / D)) & (D / 32 - 1)) << 2; }
-
-// Direct global -> LDS copies (global_load_lds_dwordx4).  A wave instruction
-// writes 1 KiB of consecutive LDS starting at M0 (lane L at 16 L); lane L
-// fetches the global chunk that the swizzle places there.
-//
-// They are issued from inline assembly on purpose: the compiler cannot tell
-// which LDS bytes such a load writes, and would otherwise drain every one of
-// them (s_waitcnt vmcnt(0)) before the next transposed LDS read, i.e. in the
-// middle of the tile that overlaps them.  The instruction writes no VGPR, so
-// no register can be reused under it; the kernel itself waits for all of
-// them (wait_all_vmem) before the barrier that publishes the tile, and
-// vector-memory loads retire in order, so the compiler's own waits for other
-// loads stay correct (only stricter).  M0 is written in the same block and
-// declared clobbered; s_nop 0 covers the M0-write -> LDS-DMA hazard.
-__device__ __forceinline__ void lds_dma_saddr(uint32_t voff, const void* sbase, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma_vaddr(const void* vaddr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(vaddr), "s"(lds_addr) : "memory", "m0");
-}
 
 // Per-lane layout of one tile copy: instruction i of this wave fills LDS rows
 // (wave * IPW + i) * RPI .. + RPI - 1 of the tile.

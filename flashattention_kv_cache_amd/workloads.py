@@ -384,3 +384,97 @@ WINDOW_DECODE = DecodeWorkload("sliding-window paged decode bf16, B=128 Hq=32 Hk
 # table (same seed), one byte per cached number.
 FP8_DECODE = DecodeWorkload("paged decode, bf16 queries, FP8 E4M3 cache, B=128 Hq=32 Hkv=8 d=128 bs=16 "
                             "L~U[512,32768]", 128, 32, 8, 128, 512, 32768, True, "fp8", 1004)
+
+
+@dataclass
+class MlaInputs:
+    """MLA decode: queries [absorbed latent query ; position query] per head and
+    one cache row [latent ; position key] per token (no head axis)."""
+    q: torch.Tensor                 # (B, Hq, d_c + d_r) bf16
+    kv: torch.Tensor                # contiguous (B, S_cap, d_c + d_r) or pool (nb, bs, d_c + d_r)
+    seq_lens: torch.Tensor          # (B,) int32
+    block_table: Optional[torch.Tensor]
+    block_size: int
+    kv_capacity: int
+    max_seq_len: int
+
+    def kv_bytes(self) -> int:
+        return int(self.seq_lens.to(torch.int64).sum()) * self.kv.shape[-1] * self.kv.element_size()
+
+
+def make_mla_inputs(B, Hq, d_c, d_r, seed, len_range=None, seq_lens=None, paged=True, block_size=64,
+                    s_cap: Optional[int] = None, spare_blocks: int = 0) -> MlaInputs:
+    """Seeded MLA decode inputs, drawn like the decode inputs (N(0,1) rounded
+    to bf16; lengths uniform and inclusive; a permuted pool with -1 padding and
+    NaN in every slot no sequence owns)."""
+    g = torch.Generator().manual_seed(seed)
+    if seq_lens is None:
+        lo, hi = len_range
+        lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64)
+        max_seq_len = hi
+    else:
+        lens = torch.tensor(list(seq_lens), dtype=torch.int64)
+        max_seq_len = int(lens.max()) if B > 0 else 0
+    w = d_c + d_r
+    q = _normal(g, (B, Hq, w), "bf16")
+    if not paged:
+        cap = s_cap if s_cap is not None else max_seq_len
+        kv = _normal(g, (B, cap, w), "bf16")
+        for b in range(B):
+            kv[b, int(lens[b]):] = float("nan")
+        return MlaInputs(q, kv, lens.to(torch.int32), None, 0, cap, max_seq_len)
+    bs = block_size
+    nblk = [(int(L) + bs - 1) // bs for L in lens]
+    total = sum(nblk) + spare_blocks
+    perm = torch.randperm(total, generator=g)
+    mb = max(1, (max_seq_len + bs - 1) // bs)
+    table = torch.full((B, mb), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]].to(torch.int32)
+        off += nblk[b]
+    kv = _normal(g, (total, bs, w), "bf16")
+    for b in range(B):
+        L = int(lens[b])
+        if L % bs:
+            kv[int(table[b, nblk[b] - 1]), L % bs:] = float("nan")
+    for p in perm[sum(nblk):].tolist():
+        kv[p] = float("nan")
+    return MlaInputs(q, kv, lens.to(torch.int32), table, bs, total, max_seq_len)
+
+
+@dataclass(frozen=True)
+class MlaWorkload:
+    name: str
+    B: int
+    Hq: int
+    d_c: int
+    d_r: int
+    d_head: int
+    len_lo: int
+    len_hi: int
+    block_size: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        """1 / sqrt(d_head + d_r): the score's denominator uses the combined
+        width of the content and position parts."""
+        return 1.0 / math.sqrt(self.d_head + self.d_r)
+
+    def flops(self, seq_lens) -> int:
+        """Per head and cached token: (d_c + d_r) multiply-adds for the score and
+        d_c for the weighted sum; 2 flop each."""
+        return 2 * self.Hq * (2 * self.d_c + self.d_r) * int(sum(int(L) for L in seq_lens))
+
+
+def mla_inputs(w: MlaWorkload) -> MlaInputs:
+    return make_mla_inputs(w.B, w.Hq, w.d_c, w.d_r, w.seed, len_range=(w.len_lo, w.len_hi), paged=True,
+                           block_size=w.block_size)
+
+
+# DeepSeek-V3-shaped MLA decode batch: 128 heads of width 128 over a 512-wide
+# latent plus a 64-wide position key, 128 sequences of 1K-16K cached tokens,
+# pages of 64 tokens.
+MLA_DECODE = MlaWorkload("MLA decode bf16, B=128 Hq=128 d_c=512 d_r=64 (d_head 128) L~U[1024,16384] bs=64",
+                         128, 128, 512, 64, 128, 1024, 16384, 64, 1008)

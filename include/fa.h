@@ -243,6 +243,47 @@ int fa_kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* 
                      int B, int Hkv, int n_new, int d, float k_scale, float v_scale, void* stream);
 
 /*
+ * fa_mla_decode — multi-head latent attention decode, in the absorbed form:
+ * every query head attends one shared cache row per token, [c ; k^R] (the
+ * latent, d_c numbers, and the decoupled position key, d_r numbers), with its
+ * query [q^lat ; q^R], and outputs the softmax-weighted sum of the latents c
+ * (in latent space; the caller applies the value up-projection W^UV).
+ *
+ * Defined by: "Module 09: Efficient Attention", sections "Multi-head Latent
+ * Attention: A Different Lever", "The Math: Compress, Reconstruct, Decouple"
+ * (the cache keeps d_c + d_r numbers per token and no head axis; per-head
+ * keys are [W^UK c ; k^R]) and "Why RoPE Has To Be Decoupled" (the content
+ * up-projections absorb into the query: q^C . W^UK c = (W^UK^T q^C) . c).
+ * The caller forms q^lat = W^UK^T q^C and applies RoPE to q^R and k^R; scale
+ * is 1 / sqrt(d_head + d_r) for the page's model ("Common Pitfalls" item 7).
+ *
+ *   q            (B, Hq, d_c + d_r) bf16: [q^lat ; q^R] per head
+ *   kv_cache     contiguous: (B, kv_capacity, d_c + d_r); paged:
+ *                (kv_capacity, block_size, d_c + d_r) pool, bf16 rows [c ; k^R]
+ *   seq_lens, block_table, block_size, max_blocks_per_seq, max_seq_len: as
+ *                fa_decode (one shared row per token instead of Hkv heads)
+ *   o            (B, Hq, d_c) bf16 output
+ *   lse          (B, Hq) fp32 output or NULL
+ *   split_tokens 0 = library choice (fa_mla_decode_split_tokens), else a
+ *                multiple of 32
+ *   workspace    fa_mla_decode_workspace_bytes(...) bytes (NULL if 0)
+ *
+ * Contract: d_c = 512 and d_r = 64 (the shape built); 0 <= L_b <= max_seq_len;
+ * block ids read in [0, kv_capacity).  Device-side violations give NaN rows
+ * and no out-of-range read, as for fa_decode.
+ */
+int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, const int32_t* block_table,
+                  int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len,
+                  void* o, float* lse, int B, int Hq, int d_c, int d_r, float scale,
+                  int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tokens per split fa_mla_decode uses when called with split_tokens = 0 (0 for rejected sizes). */
+int fa_mla_decode_split_tokens(int B, int Hq, int d_c, int d_r, int max_seq_len);
+
+/* Workspace bytes fa_mla_decode needs (0 when every sequence fits in one split or the sizes are rejected). */
+size_t fa_mla_decode_workspace_bytes(int B, int Hq, int d_c, int d_r, int max_seq_len, int split_tokens);
+
+/*
  * fa_chunked_prefill — attention of the Nq newest tokens of each sequence
  * against that sequence's whole KV cache (its own new keys included, appended
  * beforehand, e.g. by fa_kv_append): the prefill of one chunk of a long prompt,

@@ -17,6 +17,9 @@ Modules:
   paged      the paged pool: free-list block allocation, token append through
              the block table, prefix sharing, and chunked prefill (the newest
              Nq tokens of each sequence against its whole cache).
+  mla        multi-head latent attention decode: the latent-space form the
+             kernel computes, and the head-by-head form built from the page's
+             equations (the absorption identity pins one against the other).
   fp8        FP8 (E4M3) caches: the code -> value table from the bit layout,
              round-to-nearest-even quantisation with saturation, per-tensor
              scales, decode against an FP8 cache, quantising append.
@@ -32,6 +35,8 @@ from .kv_bytes import kv_cache_bytes, kv_bytes_per_token
 from .paged import (BlockAllocator, PagedSequence, append_token, share_prefix, append_batch,
                     append_batch_contiguous, chunked_prefill)
 from .fp8 import e4m3_value, decode_codes, quantize_e4m3, decode_fp8, append_fp8
+from .mla import (mla_cache_numbers, mha_cache_numbers, equivalent_gqa_groups, absorb_query,
+                  mla_decode_latent, mla_decode_explicit, latent_to_head)
 
 __all__ = [
     "kv_head_of", "causal_key_limit", "window_key_start", "attention_rows", "prefill", "prefill_rows",
@@ -41,4 +46,6 @@ __all__ = [
     "BlockAllocator", "PagedSequence", "append_token", "share_prefix", "append_batch",
     "append_batch_contiguous", "chunked_prefill",
     "e4m3_value", "decode_codes", "quantize_e4m3", "decode_fp8", "append_fp8",
+    "mla_cache_numbers", "mha_cache_numbers", "equivalent_gqa_groups", "absorb_query",
+    "mla_decode_latent", "mla_decode_explicit", "latent_to_head",
 ]

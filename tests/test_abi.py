@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_abi_version", "fa_decode_split_tokens", "fa_kv_append",
-                 "fa_chunked_prefill", "fa_decode_fp8", "fa_kv_append_fp8"):
+                 "fa_chunked_prefill", "fa_decode_fp8", "fa_kv_append_fp8", "fa_mla_decode",
+                 "fa_mla_decode_split_tokens", "fa_mla_decode_workspace_bytes"):
         assert want in names
 
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol(fa):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(fa.SIGNATURES) == set(declared_functions())
-    assert L.fa_abi_version() == 4
+    assert L.fa_abi_version() == 5
 
 
 def test_status_strings(fa):
@@ -276,6 +277,45 @@ def test_kv_append_fp8_rejects(fa, kw, status, msg):
 def test_fp8_empty_calls_are_noops(fa):
     assert decode_fp8(fa, q=0, k=0, v=0, lens=0, o=0, lse=0, B=0) == FA_OK
     assert append_fp8(fa, kn=0, vn=0, k=0, v=0, lens=0, n=0) == FA_OK
+
+
+def mla(fa, q=A, kv=A, lens=A, table=None, bs=64, mbps=4, cap=256, maxlen=256, o=A, lse=A, B=2, Hq=128, dc=512,
+        dr=64, scale=0.07, split=0, ws=None, ws_bytes=0):
+    P = ctypes.c_void_p
+    return fa.lib().fa_mla_decode(P(q), P(kv), P(lens), P(table), bs, mbps, cap, maxlen, P(o), P(lse), B, Hq, dc,
+                                  dr, scale, split, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dc=256), FA_ERR_UNSUPPORTED, "512 + 64"),
+    (dict(dr=32), FA_ERR_UNSUPPORTED, "512 + 64"),
+    (dict(Hq=0), FA_ERR_INVALID, "Hq"),
+    (dict(B=-3), FA_ERR_INVALID, "B=-3"),
+    (dict(split=100), FA_ERR_INVALID, "multiple of 32"),
+    (dict(scale=0.0), FA_ERR_INVALID, "scale"),
+    (dict(table=A, bs=48), FA_ERR_INVALID, "power of two"),
+    (dict(table=A, bs=64, mbps=3), FA_ERR_INVALID, "max_blocks_per_seq"),
+    (dict(cap=100), FA_ERR_INVALID, "capacity"),
+    (dict(q=0), FA_ERR_INVALID, "null"),
+    (dict(kv=MIS), FA_ERR_INVALID, "aligned"),
+    (dict(maxlen=4096, cap=4096, split=256), FA_ERR_INVALID, "workspace"),
+])
+def test_mla_decode_rejects(fa, kw, status, msg):
+    assert mla(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_mla_workspace_and_split_contract(fa):
+    L = fa.lib()
+    assert L.fa_mla_decode_workspace_bytes(2, 128, 512, 64, 256, 256) == 0
+    n = L.fa_mla_decode_workspace_bytes(2, 128, 512, 64, 1024, 256)
+    slots = 2 * 128 * 4
+    assert n == ((slots * 512 * 4 + 255) // 256) * 256 + ((slots * 4 + 255) // 256) * 256
+    assert L.fa_mla_decode_workspace_bytes(2, 128, 256, 64, 1024, 256) == 0
+    st = L.fa_mla_decode_split_tokens(128, 128, 512, 64, 16384)
+    assert st >= 1024 and st % 256 == 0
+    assert L.fa_mla_decode_split_tokens(128, 128, 500, 64, 16384) == 0
+    assert mla(fa, q=0, kv=0, lens=0, o=0, lse=0, B=0) == FA_OK
 
 
 def test_no_cpu_fallback_without_gpu(fa):
