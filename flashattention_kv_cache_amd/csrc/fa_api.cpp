@@ -102,11 +102,13 @@ int decode_span(int max_seq_len, int window) {
 }
 
 // MLA decode: a split writes 512 fp32 per head (256 KiB for 128 heads), so
-// splits are long: about two workgroups per CU if every sequence had
-// max_seq_len tokens, and never under 1024 tokens.  Multiples of 256.
+// splits are long: about 2.7 workgroups per CU (one workgroup fills a CU) if
+// every sequence had max_seq_len tokens, and never under 1024 tokens.
+// Multiples of 256.  Measured on MI355X: 3072 for 128 sequences of up to
+// 16384 tokens with 128 heads.
 int choose_mla_split_tokens(int B, int Hq, int max_seq_len) {
   const double groups = (double)B * ((Hq + 127) / 128);
-  long long st = (long long)(groups * max_seq_len / 512.0);
+  long long st = (long long)(groups * max_seq_len / 704.0);
   st = (st + 255) / 256 * 256;
   if (st < 1024) st = 1024;
   if (st > 16384) st = 16384;

@@ -23,10 +23,14 @@
 //     32 would need 256 accumulators alone;
 //   * 32-key tiles of cache rows go HBM -> LDS with global_load_lds_dwordx4,
 //     double buffered; one tile serves both products (V is a prefix of K);
-//   * rows are 72 sixteen-byte units; unit u of row r sits at u ^ s(r) with
-//     s(r) the bit-reversed (r >> 1) & 7, which keeps both the K operand reads
-//     (16 rows at one unit) and the transposed V reads (8 rows x 2 units) free
-//     of bank conflicts on the 64-bank LDS;
+//   * rows are 72 sixteen-byte units; unit u of row r sits at u ^ (r % 8)
+//     (low three bits only).  Measured with the LDS bank-conflict counter on
+//     MI355X, this keeps both the K operand reads (16 rows at one unit) and
+//     the transposed V reads (8 rows x 2 units) free of conflicts at this
+//     1152-byte row stride, where other XOR patterns conflict 2- to 4-way;
+//   * three tile buffers: tile t + 2 loads while tile t is computed, one
+//     barrier per tile; a split's block ids are staged in LDS first, so no
+//     vector-memory wait of the loop can stall on tile loads in flight;
 //   * the S^T accumulator gives a lane keys 4 g + i and 16 + 4 g + i (g = lane
 //     / 16) of its head: packed in that order they are the B operand of PV as
 //     they stand, and the transposed V reads fetch the same key rows;
@@ -47,24 +51,24 @@ constexpr int kHeadsWave = 16, kHeadsWG = kHeadsWave * kWaves;  // 16 per wave, 
 constexpr int kKS = kDK / 32;                         // k-steps of S^T = K Q^T (18)
 constexpr int kDB = kDC / 16;                         // 16-row blocks of O^T (32)
 constexpr int kInstr = kBN * kUnits / 64;             // direct loads per tile (36)
+constexpr int kBufs = 3;                              // tile buffers
+constexpr int kMaxEntries = 1040;                     // staged block ids (16384 tokens / 16 + slack)
 constexpr float kSlack = 8.f;                         // log2 units a running max may lag
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Physical unit of logical unit u in row r: only the low three bits move.
-__device__ __forceinline__ int swz(int r) {
-  const int x = (r >> 1) & 7;
-  return ((x & 1) << 2) | (x & 2) | (x >> 2);
-}
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
-struct Smem {
-  uint16_t kv[2][kBN * kDK];  // 2 x 36 KiB
+struct alignas(16) Smem {
+  uint16_t kv[kBufs][kBN * kDK];  // 3 x 36 KiB
+  int32_t ent[kMaxEntries];       // block ids of the split (paged, block_size >= 16)
 };
 
 // Waves issue the 36 direct loads of a tile round-robin: wave w takes loads
 // w, w + 8, ...; waves 0-3 issue 5, waves 4-7 issue 4.  s_waitcnt vmcnt(n),
 // other counters not waited: all but this wave's last n vector-memory
-// operations are done.
+// operations (one tile's loads) are done.
 __device__ __forceinline__ void wait_all_but_last_tile(int wave) {
   if (wave < kInstr % kWaves) __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves + 1));
   else __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves));
@@ -95,6 +99,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 32);
   }
+  // Drain here: otherwise the compiler's waits for these loads land inside
+  // the tile loop, where (blind to the direct loads in flight) they would
+  // drain the next tiles' loads every iteration.
+  wait_all_vmem();
   f32x4 oacc[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -110,10 +118,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv);
   const int32_t* trow = a.block_table ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
   const int bs = a.block_size, lbs = a.log2_block_size;
-  const bool blocky = trow == nullptr || bs >= 16;
+  // paged with blocks of >= 16 tokens: the split's block ids go to LDS once
+  // (validated there); the tile loads then read them from LDS
+  const int e_lo = trow && n_tiles > 0 ? t_begin >> lbs : 0;
+  const int n_ent = trow && n_tiles > 0 ? ((t_end - 1) >> lbs) - e_lo + 1 : 0;
+  const bool staged = trow && bs >= 16 && n_ent <= kMaxEntries;
+  const bool blocky = trow == nullptr || staged;
+  if (staged) {
+    for (int i = threadIdx.x; i < n_ent; i += kThreads) {
+      int e = trow[e_lo + i];
+      if (e < 0 || e >= a.kv_capacity) { bad = true; e = 0; }
+      sm.ent[i] = e;
+    }
+  }
   auto lds_of = [&](int buf) { return (uint32_t)(uintptr_t)(const lds_u16*)sm.kv[buf]; };
-  auto entry = [&](int tok) { return trow[min(tok, t_end - 1) >> lbs]; };
-  auto copy_tile = [&](int t, int buf, int e0, int e1) {
+  auto entry = [&](int tok) { return sm.ent[(min(tok, t_end - 1) >> lbs) - e_lo]; };
+  auto copy_tile = [&](int t, int buf) {
     const int tok0 = t_begin + t * kBN;
     const uint32_t lds0 = lds_of(buf);
     // The per-lane unit arithmetic below is cheap; recomputing it per tile
@@ -121,11 +141,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     if (blocky && tok0 + kBN <= t_end) {
+      int e0 = 0, e1 = 0;
       if (trow) {
-        e0 = __builtin_amdgcn_readfirstlane(e0);
-        e1 = __builtin_amdgcn_readfirstlane(e1);
-        if (e0 < 0 || e0 >= a.kv_capacity) { bad = true; e0 = 0; }
-        if (bs == 16 && (e1 < 0 || e1 >= a.kv_capacity)) { bad = true; e1 = 0; }
+        e0 = __builtin_amdgcn_readfirstlane(entry(tok0));
+        e1 = __builtin_amdgcn_readfirstlane(entry(tok0 + 16));
       }
 #pragma unroll
       for (int k = 0; k < (kInstr + kWaves - 1) / kWaves; ++k) {
@@ -187,30 +206,31 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) vbase[q] = vrow * kDK + (((2 * q + (va >> 1)) ^ swz(vrow)) << 3) + 4 * (va & 1);
 
-  // ---- prologue: tiles 0 and 1
-  int e0 = 0, e1 = 0;
-  const bool look = trow && blocky;
-  if (n_tiles > 0) {
-    copy_tile(0, 0, look ? entry(t_begin) : 0, look ? entry(t_begin + 16) : 0);
-    if (n_tiles > 1) copy_tile(1, 1, look ? entry(t_begin + kBN) : 0, look ? entry(t_begin + kBN + 16) : 0);
-  }
-  wait_all_vmem();
+  // ---- prologue: block ids visible, tiles 0 and 1 in flight
   __syncthreads();
+  if (n_tiles > 0) copy_tile(0, 0);
+  if (n_tiles > 1) copy_tile(1, 1);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (look && t + 2 < n_tiles) {  // block ids of tile t + 2, landing during this tile
-      e0 = entry(t_begin + (t + 2) * kBN);
-      e1 = entry(t_begin + (t + 2) * kBN + 16);
-    }
+    const int buf = t % kBufs;
+    // this wave's loads of tile t are done (only tile t + 1's are younger) ...
+    if (t + 1 < n_tiles) wait_all_but_last_tile(wave);
+    else wait_all_vmem();
+    // ... and every wave's; every wave is also past tile t - 1, whose buffer
+    // tile t + 2 now takes
+    __syncthreads();
+    if (t + 2 < n_tiles) copy_tile(t + 2, (t + 2) % kBufs);
     if (wave_live) {
+      // the tile's base, stated 16-byte aligned so that the K operand reads
+      // stay single ds_read_b128 (the compiler loses it through t % 3)
+      const uint16_t* tile = static_cast<const uint16_t*>(__builtin_assume_aligned(sm.kv[buf], 16));
       // S^T = K Q^T: keys 16 kb + 4 g + i of head col in sacc[kb][i]
       f32x4 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.kv[buf][kbase[kb][ks & 1] + 64 * (ks >> 1)]);
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(tile + kbase[kb][ks & 1] + 64 * (ks >> 1));
           sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb],
                                                              0, 0, 0);
         }
@@ -254,20 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         const int off = vbase[db & 3] + 64 * (db >> 2);
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.kv[buf] + off));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.kv[buf] + off + 16 * kDK));
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off + 16 * kDK));
         const bf16x8_t va8 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va8, pc, oacc[db], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with buffer buf
-    if (t + 2 < n_tiles) {
-      copy_tile(t + 2, buf, e0, e1);
-      wait_all_but_last_tile(wave);  // tile t + 1 has landed (this wave's loads)
-    } else {
-      wait_all_vmem();
-    }
-    __syncthreads();  // ... and every wave's
   }
 
   // ---- epilogue
