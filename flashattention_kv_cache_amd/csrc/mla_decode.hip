@@ -22,7 +22,7 @@
 //     32 keys).  Sixteen heads per wave keep the wave within 256 registers;
 //     32 would need 256 accumulators alone;
 //   * 32-key tiles of cache rows go HBM -> LDS with global_load_lds_dwordx4,
-//     double buffered; one tile serves both products (V is a prefix of K);
+//     one tile serves both products (V is a prefix of K);
 //   * rows are 72 sixteen-byte units; unit u of row r sits at u ^ (r % 8)
 //     (low three bits only).  Measured with the LDS bank-conflict counter on
 //     MI355X, this keeps both the K operand reads (16 rows at one unit) and
