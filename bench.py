@@ -36,6 +36,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["flashattention_kv_cache_amd/csrc/prefill_bf16.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
     "decode": ["flashattention_kv_cache_amd/csrc/decode.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
+    "mla": ["flashattention_kv_cache_amd/csrc/mla_decode.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
 }
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "prefill TFLOP/s & decode KV GB/s (% of MI355X peak), GQA d=128 bf16"
@@ -238,10 +239,13 @@ def extras(dev, steps: int, dec):
     out["mla_decode"] = {"workload": wm.name, "value": round(tf, 3), "unit": "TFLOP/s", "kernel_ms": round(m_avg, 5),
                          "kernel_ms_median": round(m_med, 5), "flops": mflops, "bytes": mbytes, "split_tokens": st,
                          "hbm_GBps": round(gbs, 2),
-                         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
-                                      "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         # 1152 B and 278528 flop per cached token (242 flop/B) sit below the
+                         # ridge point (2.5e15 / 8e12 = 312 flop/B): the floor is HBM time
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                       "kernel": "mla_split_kernel + mla_merge_kernel",
-                                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                                      "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                      "traffic": measured_traffic("mla")}}
     del mq, mkv, mo
     return out
 
