@@ -389,6 +389,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       pending = false;
     }
 
+    // Operands of group j of the interleave below (QK^T k-step j % KS of
+    // key block j / KS, and PV MFMA j), read from LDS one group ahead of
+    // their MFMAs so that no MFMA waits for an LDS read it just issued.
+    auto k_operand = [&](int j) {
+      return *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(j / KS, j % KS)]);
+    };
+    auto v_operand = [&](int j) {
+      const int kk = j / DB, db = j % DB;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t ka_n = k_operand(0), va_n{};
+    if (with_pv) va_n = v_operand(0);
+
     // ---- running max of tile t; a rescale it calls for applies to l now and
     // to O at the start of the next stage, after PV(t-1).
     if (t >= n_clean || t < n_lo) mask(sc, t);
@@ -411,42 +426,41 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     }
     const float mu = (m == -INFINITY) ? 0.f : m;
 
-    // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t)
+    // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t),
+    // packed to bf16 pairs as they are made.  PV(t-1) has 4 * DB = 2 * KS
+    // MFMAs, as many as QK^T: one per k-step.
+    u32x4_t w[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(kb, ks)]);
-        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sn[kb], 0, 0, 0);
-        if (with_pv) {
-          // PV(t-1) has 4 * DB = 2 * KS MFMAs, as many as QK^T: one per k-step.
-          const int j = kb * KS + ks;
-          const int kk = j / DB, db = j % DB;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[kk], oacc[db], 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < VPS; ++j) {
-          const int r = ks * VPS + j;
-          p[r] = fast_exp2(fmaf(sc[kb][r], c, -mu));
-          if (j & 1) l1 += p[r]; else l0 += p[r];
-        }
-        // interleave: LDS operand reads, the two MFMAs, then vector work
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU incl. transcendental
+    for (int j = 0; j < 2 * KS; ++j) {
+      const int kb = j / KS, ks = j % KS;
+      const bf16x8_t ka = ka_n, va = va_n;
+      if (j + 1 < 2 * KS) {
+        ka_n = k_operand(j + 1);
+        if (with_pv) va_n = v_operand(j + 1);
       }
+      sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sn[kb], 0, 0, 0);
+      if (with_pv) oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[j / DB], oacc[j % DB], 0, 0, 0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4_t w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[half * 8 + 2 * i], p[half * 8 + 2 * i + 1]);
-        pin(w);
-        pc[kb * 2 + half] = __builtin_bit_cast(bf16x8_t, w);
+      for (int i = 0; i < VPS; i += 2) {
+        const int r = ks * VPS + i;  // register r of block kb: element r % 8 of half r / 8
+        const float p0 = fast_exp2(fmaf(sc[kb][r], c, -mu));
+        const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c, -mu));
+        l0 += p0;
+        l1 += p1;
+        w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
       }
+      // interleave: next group's LDS reads, then each MFMA followed by half
+      // of the vector work
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // VALU incl. transcendental
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pin(w[i]);
+      pc[i] = __builtin_bit_cast(bf16x8_t, w[i]);
     }
     pin(l0);
     pin(l1);
