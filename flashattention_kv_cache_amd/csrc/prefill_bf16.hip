@@ -11,7 +11,11 @@
 // unnormalised-accumulator form (one division at the end).
 //
 // gfx950 mapping (not from the pages):
-//   * workgroup = 4 waves = 128 query rows; each wave owns 32 rows.  Key and
+//   * workgroup = 8 waves = 256 query rows, one workgroup per CU (two waves
+//     per SIMD); each wave owns 32 rows.  Both waves of a SIMD belong to the
+//     same workgroup, so neither can starve the other (two co-resident
+//     workgroups were measured to progress at rates ~1.4x apart, leaving each
+//     CU's last stretch to a single workgroup).  Key and
 //     value tiles of 64 rows go from HBM straight into LDS with
 //     global_load_lds_dwordx4 (no staging registers, no vector ALU work),
 //     issued from inline assembly so that nothing waits for them before the
@@ -39,9 +43,11 @@
 //     V(t) fly during the whole stage.  One barrier per tile.
 //   * causal: only key tiles left of and on the diagonal are visited, the mask
 //     is evaluated only on tiles that cross the diagonal or the key tail, and
-//     the grid is ordered longest query tiles first; workgroups that share a
-//     KV head are placed on the same XCD (dispatch is round-robin over the 8
-//     XCDs) so that head's K/V stays in that XCD's L2.
+//     a workgroup runs two query tiles, qb and nqb - 1 - qb, whose key-tile
+//     counts add up to the same total for every pair, so all workgroups of a
+//     launch carry equal work; workgroups that share a KV head are placed on
+//     the same XCD (dispatch is round-robin over the 8 XCDs) so that head's
+//     K/V stays in that XCD's L2.
 //   * the row sum is accumulated in fp32 from the unrounded weights (a sum of
 //     the bf16-rounded weights would move the log-sum-exp by ~1e-3 on short
 //     rows).
@@ -52,9 +58,11 @@
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup
+constexpr int kWaves = 8;              // waves per workgroup, 32 query rows each
+constexpr int kBM = 32 * kWaves;        // query rows per workgroup
 constexpr int kBN = 64;   // keys per tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCopyRows = kBN / kWaves;  // tile rows one wave copies
 constexpr float kSlack = 8.f;  // log2 units a running max may lag before rescaling
 
 template <int D>
@@ -80,7 +88,7 @@ template <int D, bool IS_V>
 struct TileCopy {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;       // rows per wave instruction
-  static constexpr int IPW = kBN / RPI / 4;  // instructions per wave
+  static constexpr int IPW = kCopyRows / RPI;  // instructions per wave
   uint32_t off[IPW];                         // byte offset of this lane's chunk within the tile
 
   __device__ void init(int wave, int lane) {
@@ -115,15 +123,15 @@ struct TileCopy {
 };
 
 // The same tile copy from a paged pool (num_blocks, block_size, Hkv, D): the
-// 16 rows a wave copies are 16 consecutive tokens.  When they sit in one block
-// (block_size >= 16 and the tile is not the sequence's last) a wave needs one
+// kCopyRows rows a wave copies are consecutive tokens.  When they sit in one
+// block (block_size >= kCopyRows and the tile is not the sequence's last) a wave needs one
 // block id and its lanes add fixed offsets to one scalar base; otherwise each
 // lane looks up the block of its own row.
 template <int D, bool IS_V>
 struct PagedCopy {
   static constexpr int CPR = D / 8;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int IPW = kBN / RPI / 4;
+  static constexpr int IPW = kCopyRows / RPI;
   uint32_t off[IPW];  // byte offset of this lane's chunk from the wave's first token
 
   __device__ void init(int wave, int lane, uint32_t slot_elems) {
@@ -135,8 +143,8 @@ struct PagedCopy {
       off[i] = (local * slot_elems + c * 8) * 2;
     }
   }
-  // Tokens tok0 .. tok0 + 15 of the sequence, all in physical block blk at
-  // slots slot0 .. slot0 + 15 (pool = slot 0 of block 0 at this KV head).
+  // Tokens tok0 .. tok0 + kCopyRows - 1 of the sequence, all in physical block
+  // blk at slots slot0 .. (pool = slot 0 of block 0 at this KV head).
   __device__ __forceinline__ void fast(const uint16_t* pool, int blk, int slot0, int bs, size_t slot_elems,
                                        const uint16_t* dst_tile, int wave) const {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u16*)dst_tile + (uint32_t)(wave * IPW * RPI * D * 2);
@@ -167,30 +175,34 @@ struct PagedCopy {
 };
 
 template <int D, bool PAGED, bool WINDOW>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a, int nqb) {
   __shared__ Smem<D> sm;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int VPS = 16 / KS; // softmax values of one 32-key block per QK^T k-step
 
-  // ---- work item: (b, h, query tile), longest first, KV-head-major per XCD
+  // ---- work item: (b, h, pair of query tiles), KV-head-major per XCD.
+  // A workgroup takes query tiles nqb - 1 - pr and pr of one head: with a
+  // causal mask their key-tile counts add up to the same total for every
+  // pair, so all workgroups carry equal work (the lone middle tile of an odd
+  // count comes last).
   const int id = blockIdx.x;
   const int n_rep = a.Hq / a.Hkv;
   const int GP = a.B * a.Hkv;
-  int b, h, qb;
+  int b, h, pr;
   if ((GP & 7) == 0) {
     const int xcd = id & 7, j = id >> 3;
-    const int per = (GP >> 3) * n_rep;  // work items per query-tile rank on one XCD
-    const int rank = j / per, rest = j % per;
+    const int per = (GP >> 3) * n_rep;  // work items per pair rank on one XCD
+    const int rest = j % per;
+    pr = j / per;
     const int gp = xcd + 8 * (rest / n_rep);
     b = gp / a.Hkv;
     h = (gp % a.Hkv) * n_rep + rest % n_rep;
-    qb = nqb - 1 - rank;
   } else {
-    const int rank = id / (a.B * a.Hq), bh = id % (a.B * a.Hq);
+    const int bh = id % (a.B * a.Hq);
+    pr = id / (a.B * a.Hq);
     b = bh / a.Hq;
     h = bh % a.Hq;
-    qb = nqb - 1 - rank;
   }
   const int g = h / n_rep;
 
@@ -198,341 +210,351 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;   // which half of the wave
   const int col = lane & 31;  // query column within the wave's 32 rows
-  const int q0 = qb * kBM;
 
   // ---- the keys: Nk of them per head, or the cached length of sequence b
   // (the queries being its newest tokens).  A length outside the contract, or
   // a block id outside the pool, turns this workgroup's rows into NaN.
   int Nk = a.Nk;
   size_t head_rows = (size_t)a.Nk;
-  bool bad = false;
+  bool bad_seq = false;
   if (a.seq_lens) {
     Nk = a.seq_lens[b];
     head_rows = (size_t)a.kv_capacity;
-    bad = Nk < 0 || Nk > a.max_seq_len || (a.causal && Nk < a.Nq);
-    if (bad) Nk = 0;
+    bad_seq = Nk < 0 || Nk > a.max_seq_len || (a.causal && Nk < a.Nq);
+    if (bad_seq) Nk = 0;
   }
   const int off = Nk - a.Nq;
-  const int last_row = min(a.Nq, q0 + kBM) - 1;
   const int W = WINDOW ? a.window : 0;  // > 0: sliding window (causal only)
-  int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
-  // first key any row of the workgroup sees (its first row's window start)
-  const int kbeg = W > 0 ? max(0, q0 + off - W + 1) : 0;
-  if (bad) kend = 0;
-  const int tb = kbeg / kBN;                              // first key tile visited
-  int te = max(tb, (kend + kBN - 1) / kBN);               // one past the last
   const int32_t* trow = PAGED ? a.block_table + (size_t)b * a.max_blocks_per_seq : nullptr;
-  if (PAGED && te > tb) {
-    // every token a copy may touch: the visited tiles, clamped to the sequence
-    const int ntok = min(te * kBN, Nk);
-    const int e0 = kbeg >> a.log2_block_size;  // blocks before the first window are never read
-    const int ne = (ntok + a.block_size - 1) >> a.log2_block_size;
-    int oob = 0;
-    for (int i = e0 + threadIdx.x; i < ne; i += kThreads) {
-      const int e = trow[i];
-      oob |= (e < 0) | (e >= a.kv_capacity);
-    }
-    if (__syncthreads_or(oob)) {
-      bad = true;
-      te = tb;
-    }
-  }
-  // tiles in [n_lo, n_clean) need no mask for any row of the workgroup
-  const int n_clean = a.causal ? min((q0 + off + 1) / kBN, Nk / kBN) : Nk / kBN;
-  const int n_lo = W > 0 ? (max(0, last_row + off - W + 1) + kBN - 1) / kBN : 0;
-
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (PAGED ? (size_t)g * D : (size_t)(b * a.Hkv + g) * head_rows * D);
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (PAGED ? (size_t)g * D : (size_t)(b * a.Hkv + g) * head_rows * D);
 
-  // ---- Q^T operand fragments, kept in registers
-  const int qrow = q0 + wave * 32 + col;
-  bf16x8_t qf[KS];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq + min(qrow, a.Nq - 1)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16 + hl * 8);
-  }
+  // One query tile: everything from the key range to the epilogue.
+  auto run_tile = [&](const int qb) {
+    const int q0 = qb * kBM;
+    bool bad = bad_seq;
+    const int last_row = min(a.Nq, q0 + kBM) - 1;
+    int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
+    // first key any row of the workgroup sees (its first row's window start)
+    const int kbeg = W > 0 ? max(0, q0 + off - W + 1) : 0;
+    if (bad) kend = 0;
+    const int tb = kbeg / kBN;                              // first key tile visited
+    int te = max(tb, (kend + kBN - 1) / kBN);               // one past the last
+    if (PAGED && te > tb) {
+      // every token a copy may touch: the visited tiles, clamped to the sequence
+      const int ntok = min(te * kBN, Nk);
+      const int e0 = kbeg >> a.log2_block_size;  // blocks before the first window are never read
+      const int ne = (ntok + a.block_size - 1) >> a.log2_block_size;
+      int oob = 0;
+      for (int i = e0 + threadIdx.x; i < ne; i += kThreads) {
+        const int e = trow[i];
+        oob |= (e < 0) | (e >= a.kv_capacity);
+      }
+      if (__syncthreads_or(oob)) {
+        bad = true;
+        te = tb;
+      }
+    }
+    // tiles in [n_lo, n_clean) need no mask for any row of the workgroup
+    const int n_clean = a.causal ? min((q0 + off + 1) / kBN, Nk / kBN) : Nk / kBN;
+    const int n_lo = W > 0 ? (max(0, last_row + off - W + 1) + kBN - 1) / kBN : 0;
 
-  f32x16_t oacc[DB];
+    // ---- Q^T operand fragments, kept in registers
+    const int qrow = q0 + wave * 32 + col;
+    bf16x8_t qf[KS];
+    {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq + min(qrow, a.Nq - 1)) * D;
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m = -INFINITY, l0 = 0.f, l1 = 0.f;
-  const float c = a.scale * kLog2e;
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16 + hl * 8);
+    }
 
-  using KCopy = typename std::conditional<PAGED, PagedCopy<D, false>, TileCopy<D, false>>::type;
-  using VCopy = typename std::conditional<PAGED, PagedCopy<D, true>, TileCopy<D, true>>::type;
-  KCopy kcp;
-  VCopy vcp;
-  const size_t slot_elems = (size_t)a.Hkv * D;  // paged: elements between consecutive slots
-  const int lbs = a.log2_block_size, bsz = a.block_size;
-  const bool one_block = bsz >= 16;             // paged: a wave's 16 tokens share a block
-  if constexpr (PAGED) {
-    kcp.init(wave, lane, (uint32_t)slot_elems);
-    vcp.init(wave, lane, (uint32_t)slot_elems);
-  } else {
-    kcp.init(wave, lane);
-    vcp.init(wave, lane);
-  }
-  // Block id of the first of the 16 tokens this wave copies from tile t
-  // (clamped to the sequence; loaded a stage ahead of its use).
-  auto entry = [&](int t) { return trow[min(max(t * kBN + wave * 16, kbeg), Nk - 1) >> lbs]; };
-  int eK = 0, eV = 0;  // paged, one_block: block ids for the next stage's K and V copies
-  // Tile t of K or V (buffer dst); e = its block id when one_block.
-  auto copy_k = [&](uint16_t* dst, int t, int e) {
+    f32x16_t oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+    float m = -INFINITY, l0 = 0.f, l1 = 0.f;
+    const float c = a.scale * kLog2e;
+
+    using KCopy = typename std::conditional<PAGED, PagedCopy<D, false>, TileCopy<D, false>>::type;
+    using VCopy = typename std::conditional<PAGED, PagedCopy<D, true>, TileCopy<D, true>>::type;
+    KCopy kcp;
+    VCopy vcp;
+    const size_t slot_elems = (size_t)a.Hkv * D;  // paged: elements between consecutive slots
+    const int lbs = a.log2_block_size, bsz = a.block_size;
+    const bool one_block = bsz >= kCopyRows;      // paged: the tokens a wave copies share a block
     if constexpr (PAGED) {
-      const int tok0 = t * kBN + wave * 16;
-      if (one_block && tok0 >= kbeg && tok0 + 16 <= Nk)
-        kcp.fast(kg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
-      else
-        kcp.slow(kg, trow, t * kBN, kbeg, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+      kcp.init(wave, lane, (uint32_t)slot_elems);
+      vcp.init(wave, lane, (uint32_t)slot_elems);
     } else {
-      kcp.copy(kg, dst, t * kBN, kbeg, Nk, wave, lane);
+      kcp.init(wave, lane);
+      vcp.init(wave, lane);
     }
-  };
-  auto copy_v = [&](uint16_t* dst, int t, int e) {
-    if constexpr (PAGED) {
-      const int tok0 = t * kBN + wave * 16;
-      if (one_block && tok0 >= kbeg && tok0 + 16 <= Nk)
-        vcp.fast(vg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
-      else
-        vcp.slow(vg, trow, t * kBN, kbeg, Nk, lbs, bsz, slot_elems, dst, wave, lane);
-    } else {
-      vcp.copy(vg, dst, t * kBN, kbeg, Nk, wave, lane);
-    }
-  };
-
-  // LDS element offset of this lane's K operand (row kb*32 + col, logical
-  // 16-byte chunk ks*2 + hl), and of its V^T transposed reads.
-  auto k_off = [&](int kb, int ks) {
-    const int row = kb * 32 + col;
-    return row * D + (((ks * 2 + hl) ^ k_swz<D>(row)) * 8);
-  };
-  // V^T operand for k-step kk (keys 16kk .. 16kk+15) and dims db*32 .. +31:
-  // lane L of 16-lane group gi reads row key(j) = 16kk + 8*half + 4*(gi/2) + j
-  // with j = (L%16)/4, at dims db*32 + 16*(gi%2) + 4*(L%4) .. +3; the
-  // transpose hands lane L the 4 keys of dim db*32 + L%32.
-  const int gi = lane >> 4, li = lane & 15;
-  auto v_off = [&](int kk, int half, int db) {
-    const int row = kk * 16 + half * 8 + (gi >> 1) * 4 + (li >> 2);
-    const int d = db * 32 + (gi & 1) * 16 + (li & 3) * 4;
-    return row * D + ((((d >> 3) ^ v_swz<D>(row)) << 3) | (d & 7));
-  };
-
-  // S^T of one tile for this wave's 32 queries: two 32-key blocks
-  auto qk = [&](f32x16_t (&sacc)[2], int buf) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.k[buf][k_off(kb, ks)]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sacc[kb], 0, 0, 0);
+    // Block id of the first of the tokens this wave copies from tile t
+    // (clamped to the sequence; loaded a stage ahead of its use).
+    auto entry = [&](int t) { return trow[min(max(t * kBN + wave * kCopyRows, kbeg), Nk - 1) >> lbs]; };
+    int eK = 0, eV = 0;  // paged, one_block: block ids for the next stage's K and V copies
+    // Tile t of K or V (buffer dst); e = its block id when one_block.
+    auto copy_k = [&](uint16_t* dst, int t, int e) {
+      if constexpr (PAGED) {
+        const int tok0 = t * kBN + wave * kCopyRows;
+        if (one_block && tok0 >= kbeg && tok0 + kCopyRows <= Nk)
+          kcp.fast(kg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
+        else
+          kcp.slow(kg, trow, t * kBN, kbeg, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+      } else {
+        kcp.copy(kg, dst, t * kBN, kbeg, Nk, wave, lane);
       }
-  };
-  // Keys past Nk and, when causal, keys right of the (bottom-right aligned)
-  // diagonal get weight 0.  Register r of block kb holds key
-  // t*64 + kb*32 + 8*(r/4) + 4*hl + r%4, so one compare against a per-lane
-  // limit decides each element.
-  // With a window, keys before the row's window start are masked the same way.
-  auto mask = [&](f32x16_t (&sacc)[2], int t) {
-    const int base = t * kBN + hl * 4;
-    const int lim = (a.causal ? min(qrow + off, Nk - 1) : Nk - 1) - base;
-    const int lo = (W > 0 ? qrow + off - W + 1 : 0) - base;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kb * 32 + (r / 4) * 8 + (r % 4);
-        if (kk > lim || (WINDOW && kk < lo)) sacc[kb][r] = -INFINITY;
-      }
-  };
-
-  bool pending = false;  // wave-uniform: a rescale of O is due
-  float pend_alpha = 1.f;
-
-  // O^T += V(t)^T P(t) for the V tile in buffer vb (16 MFMAs).
-  auto pv = [&](const bf16x8_t (&pp)[4], int vb) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[vb] + v_off(kk, 0, db)));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[vb] + v_off(kk, 1, db)));
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[kk], oacc[db], 0, 0, 0);
-      }
-  };
-
-  // One pipeline stage t: softmax of tile t (scores in sc, weights out to pc)
-  // on the vector ALUs, while the matrix cores run QK^T of tile t+1 (into sn)
-  // and PV of tile t-1 (weights pp, V in buffer (t-1)&1).  The direct loads
-  // of K(t+2) and V(t) fly during the whole stage.
-  auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
-                   bool with_pv) {
-    const int kb_next = (t + 1) & 1;  // K(t+1)
-    if (t + 2 < te) copy_k(sm.k[t & 1], t + 2, eK);
-    copy_v(sm.v[t & 1], t, eV);
-    if (PAGED && one_block) {
-      eK = entry(t + 3);
-      eV = entry(t + 1);
-      asm volatile("" ::: "memory");  // the lookups fly during this stage
-    }
-
-    // A rescale decided in the previous stage applies to O once PV(t-2) (its
-    // weights used the old reference) is in, i.e. now, before PV(t-1) starts.
-    if (pending) {
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
-      pending = false;
-    }
-
-    // Operands of group j of the interleave below (QK^T k-step j % KS of
-    // key block j / KS, and PV MFMA j), read from LDS one group ahead of
-    // their MFMAs so that no MFMA waits for an LDS read it just issued.
-    auto k_operand = [&](int j) {
-      return *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(j / KS, j % KS)]);
     };
-    auto v_operand = [&](int j) {
-      const int kk = j / DB, db = j % DB;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    auto copy_v = [&](uint16_t* dst, int t, int e) {
+      if constexpr (PAGED) {
+        const int tok0 = t * kBN + wave * kCopyRows;
+        if (one_block && tok0 >= kbeg && tok0 + kCopyRows <= Nk)
+          vcp.fast(vg, __builtin_amdgcn_readfirstlane(e), tok0 & (bsz - 1), bsz, slot_elems, dst, wave);
+        else
+          vcp.slow(vg, trow, t * kBN, kbeg, Nk, lbs, bsz, slot_elems, dst, wave, lane);
+      } else {
+        vcp.copy(vg, dst, t * kBN, kbeg, Nk, wave, lane);
+      }
     };
-    bf16x8_t ka_n = k_operand(0), va_n{};
-    if (with_pv) va_n = v_operand(0);
 
-    // ---- running max of tile t; a rescale it calls for applies to l now and
-    // to O at the start of the next stage, after PV(t-1).
-    if (t >= n_clean || t < n_lo) mask(sc, t);
-    float mx = sc[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    mx = halves_max(mx) * c;
-    // Rescale only when some row's max grows by more than kSlack (log2
-    // units): (m, l, O) stays exact for any reference m within kSlack of the
-    // true max, and P is then at most 2^kSlack (fine in bf16).
-    const float mn = fmaxf(m, mx);
-    if (__any(mn > m + kSlack)) {
-      pend_alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
-      pending = true;
-      l0 *= pend_alpha;
-      l1 *= pend_alpha;
-      m = mn;
-    }
-    const float mu = (m == -INFINITY) ? 0.f : m;
+    // LDS element offset of this lane's K operand (row kb*32 + col, logical
+    // 16-byte chunk ks*2 + hl), and of its V^T transposed reads.
+    auto k_off = [&](int kb, int ks) {
+      const int row = kb * 32 + col;
+      return row * D + (((ks * 2 + hl) ^ k_swz<D>(row)) * 8);
+    };
+    // V^T operand for k-step kk (keys 16kk .. 16kk+15) and dims db*32 .. +31:
+    // lane L of 16-lane group gi reads row key(j) = 16kk + 8*half + 4*(gi/2) + j
+    // with j = (L%16)/4, at dims db*32 + 16*(gi%2) + 4*(L%4) .. +3; the
+    // transpose hands lane L the 4 keys of dim db*32 + L%32.
+    const int gi = lane >> 4, li = lane & 15;
+    auto v_off = [&](int kk, int half, int db) {
+      const int row = kk * 16 + half * 8 + (gi >> 1) * 4 + (li >> 2);
+      const int d = db * 32 + (gi & 1) * 16 + (li & 3) * 4;
+      return row * D + ((((d >> 3) ^ v_swz<D>(row)) << 3) | (d & 7));
+    };
 
-    // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t),
-    // packed to bf16 pairs as they are made.  PV(t-1) has 4 * DB = 2 * KS
-    // MFMAs, as many as QK^T: one per k-step.
-    u32x4_t w[4];
+    // S^T of one tile for this wave's 32 queries: two 32-key blocks
+    auto qk = [&](f32x16_t (&sacc)[2], int buf) {
 #pragma unroll
-    for (int j = 0; j < 2 * KS; ++j) {
-      const int kb = j / KS, ks = j % KS;
-      const bf16x8_t ka = ka_n, va = va_n;
-      if (j + 1 < 2 * KS) {
-        ka_n = k_operand(j + 1);
-        if (with_pv) va_n = v_operand(j + 1);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&sm.k[buf][k_off(kb, ks)]);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sacc[kb], 0, 0, 0);
+        }
+    };
+    // Keys past Nk and, when causal, keys right of the (bottom-right aligned)
+    // diagonal get weight 0.  Register r of block kb holds key
+    // t*64 + kb*32 + 8*(r/4) + 4*hl + r%4, so one compare against a per-lane
+    // limit decides each element.
+    // With a window, keys before the row's window start are masked the same way.
+    auto mask = [&](f32x16_t (&sacc)[2], int t) {
+      const int base = t * kBN + hl * 4;
+      const int lim = (a.causal ? min(qrow + off, Nk - 1) : Nk - 1) - base;
+      const int lo = (W > 0 ? qrow + off - W + 1 : 0) - base;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kb * 32 + (r / 4) * 8 + (r % 4);
+          if (kk > lim || (WINDOW && kk < lo)) sacc[kb][r] = -INFINITY;
+        }
+    };
+
+    bool pending = false;  // wave-uniform: a rescale of O is due
+    float pend_alpha = 1.f;
+
+    // O^T += V(t)^T P(t) for the V tile in buffer vb (16 MFMAs).
+    auto pv = [&](const bf16x8_t (&pp)[4], int vb) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[vb] + v_off(kk, 0, db)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[vb] + v_off(kk, 1, db)));
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[kk], oacc[db], 0, 0, 0);
+        }
+    };
+
+    // One pipeline stage t: softmax of tile t (scores in sc, weights out to pc)
+    // on the vector ALUs, while the matrix cores run QK^T of tile t+1 (into sn)
+    // and PV of tile t-1 (weights pp, V in buffer (t-1)&1).  The direct loads
+    // of K(t+2) and V(t) fly during the whole stage.
+    auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
+                     bool with_pv) {
+      const int kb_next = (t + 1) & 1;  // K(t+1)
+      if (t + 2 < te) copy_k(sm.k[t & 1], t + 2, eK);
+      copy_v(sm.v[t & 1], t, eV);
+      if (PAGED && one_block) {
+        eK = entry(t + 3);
+        eV = entry(t + 1);
+        asm volatile("" ::: "memory");  // the lookups fly during this stage
       }
-      sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sn[kb], 0, 0, 0);
-      if (with_pv) oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[j / DB], oacc[j % DB], 0, 0, 0);
+
+      // A rescale decided in the previous stage applies to O once PV(t-2) (its
+      // weights used the old reference) is in, i.e. now, before PV(t-1) starts.
+      if (pending) {
 #pragma unroll
-      for (int i = 0; i < VPS; i += 2) {
-        const int r = ks * VPS + i;  // register r of block kb: element r % 8 of half r / 8
-        const float p0 = fast_exp2(fmaf(sc[kb][r], c, -mu));
-        const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c, -mu));
-        l0 += p0;
-        l1 += p1;
-        w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
+        pending = false;
       }
-      // interleave: next group's LDS reads, then each MFMA followed by half
-      // of the vector work
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // VALU incl. transcendental
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-    }
+
+      // Operands of group j of the interleave below (QK^T k-step j % KS of
+      // key block j / KS, and PV MFMA j), read from LDS one group ahead of
+      // their MFMAs so that no MFMA waits for an LDS read it just issued.
+      auto k_operand = [&](int j) {
+        return *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(j / KS, j % KS)]);
+      };
+      auto v_operand = [&](int j) {
+        const int kk = j / DB, db = j % DB;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8_t ka_n = k_operand(0), va_n{};
+      if (with_pv) va_n = v_operand(0);
+
+      // ---- running max of tile t; a rescale it calls for applies to l now and
+      // to O at the start of the next stage, after PV(t-1).
+      if (t >= n_clean || t < n_lo) mask(sc, t);
+      float mx = sc[0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pin(w[i]);
-      pc[i] = __builtin_bit_cast(bf16x8_t, w[i]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+      mx = halves_max(mx) * c;
+      // Rescale only when some row's max grows by more than kSlack (log2
+      // units): (m, l, O) stays exact for any reference m within kSlack of the
+      // true max, and P is then at most 2^kSlack (fine in bf16).
+      const float mn = fmaxf(m, mx);
+      if (__any(mn > m + kSlack)) {
+        pend_alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
+        pending = true;
+        l0 *= pend_alpha;
+        l1 *= pend_alpha;
+        m = mn;
+      }
+      const float mu = (m == -INFINITY) ? 0.f : m;
+
+      // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t),
+      // packed to bf16 pairs as they are made.  PV(t-1) has 4 * DB = 2 * KS
+      // MFMAs, as many as QK^T: one per k-step.
+      u32x4_t w[4];
+#pragma unroll
+      for (int j = 0; j < 2 * KS; ++j) {
+        const int kb = j / KS, ks = j % KS;
+        const bf16x8_t ka = ka_n, va = va_n;
+        if (j + 1 < 2 * KS) {
+          ka_n = k_operand(j + 1);
+          if (with_pv) va_n = v_operand(j + 1);
+        }
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : sn[kb], 0, 0, 0);
+        if (with_pv) oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[j / DB], oacc[j % DB], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < VPS; i += 2) {
+          const int r = ks * VPS + i;  // register r of block kb: element r % 8 of half r / 8
+          const float p0 = fast_exp2(fmaf(sc[kb][r], c, -mu));
+          const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c, -mu));
+          l0 += p0;
+          l1 += p1;
+          w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+        }
+        // interleave: next group's LDS reads, then each MFMA followed by half
+        // of the vector work
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // VALU incl. transcendental
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pin(w[i]);
+        pc[i] = __builtin_bit_cast(bf16x8_t, w[i]);
+      }
+      pin(l0);
+      pin(l1);
+      wait_all_vmem();  // this wave's direct loads have landed
+      __syncthreads();  // ... and every other wave's
+    };
+
+    f32x16_t s_a[2], s_b[2];
+    bf16x8_t p_a[4], p_b[4];
+
+    // prologue: K(0) -> K buffer 0, K(1) -> K buffer 1.  The drain is
+    // unconditional so that, on every path into the loop, the Q fragments are
+    // known to have arrived (otherwise each QK^T MFMA waits on vmcnt).
+    // Tiles are numbered from the start of the sequence; the workgroup visits
+    // [tb, te) and buffer parity follows the tile number.
+    if (te > tb) {
+      const bool look = PAGED && one_block;
+      copy_k(sm.k[tb & 1], tb, look ? entry(tb) : 0);
+      if (te > tb + 1) copy_k(sm.k[(tb + 1) & 1], tb + 1, look ? entry(tb + 1) : 0);
+      if (look) {
+        eK = entry(tb + 2);
+        eV = entry(tb);
+      }
     }
-    pin(l0);
-    pin(l1);
-    wait_all_vmem();  // this wave's direct loads have landed
-    __syncthreads();  // ... and every other wave's
+    wait_all_vmem();
+    __syncthreads();
+    if (te > tb) qk(s_a, tb & 1);
+    __syncthreads();  // K buffer of tile tb is refilled by the first stage
+
+    if (te > tb) {
+      stage(s_a, s_b, p_b, p_a, tb, false);
+      int t = tb + 1;
+      for (; t + 1 < te; t += 2) {
+        stage(s_b, s_a, p_a, p_b, t, true);
+        stage(s_a, s_b, p_b, p_a, t + 1, true);
+      }
+      if (t < te) stage(s_b, s_a, p_a, p_b, t, true);
+      // drain: a due rescale, then PV of the last tile
+      if (pending) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
+      }
+      if (t < te) pv(p_b, t & 1);
+      else pv(p_a, (t - 1) & 1);
+    }
+
+    // ---- epilogue: one division, bf16 output, natural-log LSE
+    const float lt = halves_sum(l0 + l1);
+    if (qrow < a.Nq) {
+      const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = db * 32 + q4 * 8 + hl * 4;
+          u32x2_t w;
+          w[0] = pack_bf16x2(oacc[db][q4 * 4 + 0] * inv, oacc[db][q4 * 4 + 1] * inv);
+          w[1] = pack_bf16x2(oacc[db][q4 * 4 + 2] * inv, oacc[db][q4 * 4 + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(op + d) = w;
+        }
+      if (a.lse && hl == 0)
+        a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+    }
   };
-
-  f32x16_t s_a[2], s_b[2];
-  bf16x8_t p_a[4], p_b[4];
-
-  // prologue: K(0) -> K buffer 0, K(1) -> K buffer 1.  The drain is
-  // unconditional so that, on every path into the loop, the Q fragments are
-  // known to have arrived (otherwise each QK^T MFMA waits on vmcnt).
-  // Tiles are numbered from the start of the sequence; the workgroup visits
-  // [tb, te) and buffer parity follows the tile number.
-  if (te > tb) {
-    const bool look = PAGED && one_block;
-    copy_k(sm.k[tb & 1], tb, look ? entry(tb) : 0);
-    if (te > tb + 1) copy_k(sm.k[(tb + 1) & 1], tb + 1, look ? entry(tb + 1) : 0);
-    if (look) {
-      eK = entry(tb + 2);
-      eV = entry(tb);
-    }
+  run_tile(nqb - 1 - pr);
+  if (pr < nqb - 1 - pr) {
+    __syncthreads();  // the first tile's last LDS reads are done
+    run_tile(pr);
   }
-  wait_all_vmem();
-  __syncthreads();
-  if (te > tb) qk(s_a, tb & 1);
-  __syncthreads();  // K buffer of tile tb is refilled by the first stage
-
-  if (te > tb) {
-    stage(s_a, s_b, p_b, p_a, tb, false);
-    int t = tb + 1;
-    for (; t + 1 < te; t += 2) {
-      stage(s_b, s_a, p_a, p_b, t, true);
-      stage(s_a, s_b, p_b, p_a, t + 1, true);
-    }
-    if (t < te) stage(s_b, s_a, p_a, p_b, t, true);
-    // drain: a due rescale, then PV of the last tile
-    if (pending) {
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
-    }
-    if (t < te) pv(p_b, t & 1);
-    else pv(p_a, (t - 1) & 1);
-  }
-
-  // ---- epilogue: one division, bf16 output, natural-log LSE
-  const float lt = halves_sum(l0 + l1);
-  if (qrow >= a.Nq) return;
-  const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qrow) * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = db * 32 + q4 * 8 + hl * 4;
-      u32x2_t w;
-      w[0] = pack_bf16x2(oacc[db][q4 * 4 + 0] * inv, oacc[db][q4 * 4 + 1] * inv);
-      w[1] = pack_bf16x2(oacc[db][q4 * 4 + 2] * inv, oacc[db][q4 * 4 + 3] * inv);
-      *reinterpret_cast<u32x2_t*>(op + d) = w;
-    }
-  if (a.lse && hl == 0)
-    a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.Nq + kBM - 1) / kBM;
-  const long long grid = (long long)nqb * a.Hq * a.B;
+  const long long grid = (long long)((nqb + 1) / 2) * a.Hq * a.B;  // pairs of query tiles
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool paged = a.block_table != nullptr, win = a.window > 0;
 #define FA_LAUNCH(DD, PG, WN) \
