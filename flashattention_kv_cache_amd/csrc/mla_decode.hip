@@ -65,6 +65,31 @@ struct alignas(16) Smem {
   int32_t ent[kMaxEntries];       // block ids of the split (paged, block_size >= 16)
 };
 
+// MFMA steps issued from assembly, so that their order against the operand
+// reads is the one written here (the compiler would otherwise hoist all of a
+// tile's LDS reads ahead of the chain, out of registers).  Each accumulates in
+// place (destination exactly overlapping SrcC, which the hardware forwards).
+// What the compiler cannot see through the assembly is padded explicitly:
+// vector instructions read an MFMA result (or overwrite its SrcC) only after
+// mfma_done(), and an MFMA reads vector-written operands after valu_done().
+__device__ __forceinline__ void mfma_first(f32x4& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_done(f32x4 (&acc)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
+}
+__device__ __forceinline__ void valu_done(bf16x8_t& p) { asm volatile("s_nop 3" : "+v"(p)); }
+// Orders an LDS operand read after the MFMA issued before it (an empty
+// statement that claims to change the read's element offset; the pointer
+// itself must keep its LDS address space).
+__device__ __forceinline__ int after_prev(int off) {
+  asm volatile("" : "+v"(off));
+  return off;
+}
+
 // Waves issue the 36 direct loads of a tile round-robin: wave w takes loads
 // w, w + 8, ...; waves 0-3 issue 5, waves 4-7 issue 4.  s_waitcnt vmcnt(n),
 // other counters not waited: all but this wave's last n vector-memory
@@ -108,6 +133,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
   for (int i = 0; i < kDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l0 = 0.f, l1 = 0.f;
   const float c = a.scale * kLog2e;
+  // the wait states vector instructions need before touching O^T after the
+  // MFMAs that accumulate it
+  auto oacc_done = [&]() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) asm volatile("" : "+v"(oacc[i]));
+  };
 
   // ---- tile copy.  Load i of a tile fills units 64 i .. 64 i + 63 of the
   // tile's 32 x 72 units; lane L takes unit u = 64 i + L: row u / 72, physical
@@ -200,11 +232,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
     for (int par = 0; par < 2; ++par)
       kbase[kb][par] = (16 * kb + col) * kDK + (((4 * par + g) ^ swz(col)) << 3);
-  const int vj = (lane & 15) >> 2, va = lane & 3;
-  const int vrow = 4 * g + vj;
-  int vbase[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) vbase[q] = vrow * kDK + (((2 * q + (va >> 1)) ^ swz(vrow)) << 3) + 4 * (va & 1);
+  // (recomputed where used, from a lane id the compiler cannot hoist)
+  auto v_base = [&](int q) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int vrow = 4 * (ln >> 4) + ((ln & 15) >> 2), va = ln & 3;
+    return vrow * kDK + (((2 * q + (va >> 1)) ^ swz(vrow)) << 3) + 4 * (va & 1);
+  };
 
   // ---- prologue: block ids visible, tiles 0 and 1 in flight
   __syncthreads();
@@ -225,15 +259,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
       // stay single ds_read_b128 (the compiler loses it through t % 3)
       const uint16_t* tile = static_cast<const uint16_t*>(__builtin_assume_aligned(sm.kv[buf], 16));
       // S^T = K Q^T: keys 16 kb + 4 g + i of head col in sacc[kb][i]
+      // the two key blocks' chains alternate; each k-step's operands are
+      // read while the previous step's MFMAs run
+      auto k_operand = [&](int kb, int ks) {
+        const uint16_t* p = tile + after_prev(kbase[kb][ks & 1] + 64 * (ks >> 1));
+        return *static_cast<const bf16x8_t*>(__builtin_assume_aligned(p, 16));
+      };
       f32x4 sacc[2];
+      bf16x8_t ka0 = k_operand(0, 0), ka1 = k_operand(1, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(tile + kbase[kb][ks & 1] + 64 * (ks >> 1));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb],
-                                                             0, 0, 0);
-        }
+      for (int ks = 0; ks < kKS; ++ks) {
+        bf16x8_t na0 = ka0, na1 = ka1;
+        if (ks + 1 < kKS) na0 = k_operand(0, ks + 1);
+        if (ks == 0) mfma_first(sacc[0], ka0, qf[ks]);
+        else mfma_acc(sacc[0], ka0, qf[ks]);
+        if (ks + 1 < kKS) na1 = k_operand(1, ks + 1);
+        if (ks == 0) mfma_first(sacc[1], ka1, qf[ks]);
+        else mfma_acc(sacc[1], ka1, qf[ks]);
+        ka0 = na0;
+        ka1 = na1;
+      }
+      mfma_done(sacc);
       if (t == n_tiles - 1) {  // keys past the split get weight 0
         const int lim = t_end - 1 - (t_begin + t * kBN + 4 * g);
 #pragma unroll
@@ -249,6 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
       const float mn = fmaxf(m, mx);
       if (__any(mn > m + kSlack)) {
         const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
+        oacc_done();
 #pragma unroll
         for (int i = 0; i < kDB; ++i) oacc[i] *= alpha;
         l0 *= alpha;
@@ -269,20 +316,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
       w[1] = pack_bf16x2(p[0][2], p[0][3]);
       w[2] = pack_bf16x2(p[1][0], p[1][1]);
       w[3] = pack_bf16x2(p[1][2], p[1][3]);
-      const bf16x8_t pc = __builtin_bit_cast(bf16x8_t, w);
-      // O^T += V^T P^T, one k-step of 32 keys per 16-dim block
+      bf16x8_t pc = __builtin_bit_cast(bf16x8_t, w);
+      valu_done(pc);
+      // O^T += V^T P^T, one k-step of 32 keys per 16-dim block; each block's
+      // operand is read while the previous block's MFMA runs
+      int vbase[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vbase[q] = v_base(q);
+      auto v_operand = [&](int db) {
+        const uint16_t* p = tile + after_prev(vbase[db & 3] + 64 * (db >> 2));
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * kDK));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8_t va = v_operand(0);
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const int off = vbase[db & 3] + 64 * (db >> 2);
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off + 16 * kDK));
-        const bf16x8_t va8 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va8, pc, oacc[db], 0, 0, 0);
+        bf16x8_t vn = va;
+        if (db + 1 < kDB) vn = v_operand(db + 1);
+        mfma_acc(oacc[db], va, pc);
+        va = vn;
       }
     }
   }
 
   // ---- epilogue
+  oacc_done();
   const bool any_bad = __syncthreads_or(bad);
   float lt = l0 + l1;
   lt += __shfl_xor(lt, 16);
