@@ -28,7 +28,8 @@
 //     MI355X, this keeps both the K operand reads (16 rows at one unit) and
 //     the transposed V reads (8 rows x 2 units) free of conflicts at this
 //     1152-byte row stride, where other XOR patterns conflict 2- to 4-way;
-//   * three tile buffers: tile t + 2 loads while tile t is computed, one
+//   * four tile buffers: tiles t + 1 .. t + 3 load while tile t is computed
+//     (three tiles in flight per CU, what HBM latency asks for here), one
 //     barrier per tile; a split's block ids are staged in LDS first, so no
 //     vector-memory wait of the loop can stall on tile loads in flight;
 //   * the S^T accumulator gives a lane keys 4 g + i and 16 + 4 g + i (g = lane
@@ -51,7 +52,7 @@ constexpr int kHeadsWave = 16, kHeadsWG = kHeadsWave * kWaves;  // 16 per wave, 
 constexpr int kKS = kDK / 32;                         // k-steps of S^T = K Q^T (18)
 constexpr int kDB = kDC / 16;                         // 16-row blocks of O^T (32)
 constexpr int kInstr = kBN * kUnits / 64;             // direct loads per tile (36)
-constexpr int kBufs = 3;                              // tile buffers
+constexpr int kBufs = 4;                              // tile buffers
 constexpr int kMaxEntries = 1040;                     // staged block ids (16384 tokens / 16 + slack)
 constexpr float kSlack = 8.f;                         // log2 units a running max may lag
 
@@ -61,7 +62,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 
 struct alignas(16) Smem {
-  uint16_t kv[kBufs][kBN * kDK];  // 3 x 36 KiB
+  uint16_t kv[kBufs][kBN * kDK];  // 4 x 36 KiB
   int32_t ent[kMaxEntries];       // block ids of the split (paged, block_size >= 16)
 };
 
@@ -93,10 +94,17 @@ __device__ __forceinline__ int after_prev(int off) {
 // Waves issue the 36 direct loads of a tile round-robin: wave w takes loads
 // w, w + 8, ...; waves 0-3 issue 5, waves 4-7 issue 4.  s_waitcnt vmcnt(n),
 // other counters not waited: all but this wave's last n vector-memory
-// operations (one tile's loads) are done.
-__device__ __forceinline__ void wait_all_but_last_tile(int wave) {
-  if (wave < kInstr % kWaves) __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves + 1));
-  else __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves));
+// operations (the loads of its `younger` most recent tiles) are done.
+__device__ __forceinline__ void wait_all_but_last_tiles(int wave, int younger) {
+  if (wave < kInstr % kWaves) {
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kInstr / kWaves + 1)));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves + 1));
+    else wait_all_vmem();
+  } else {
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kInstr / kWaves)));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kInstr / kWaves));
+    else wait_all_vmem();
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
@@ -240,23 +248,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
     return vrow * kDK + (((2 * q + (va >> 1)) ^ swz(vrow)) << 3) + 4 * (va & 1);
   };
 
-  // ---- prologue: block ids visible, tiles 0 and 1 in flight
+  // ---- prologue: block ids visible, tiles 0 - 2 in flight
   __syncthreads();
   if (n_tiles > 0) copy_tile(0, 0);
   if (n_tiles > 1) copy_tile(1, 1);
+  if (n_tiles > 2) copy_tile(2, 2);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t % kBufs;
-    // this wave's loads of tile t are done (only tile t + 1's are younger) ...
-    if (t + 1 < n_tiles) wait_all_but_last_tile(wave);
-    else wait_all_vmem();
+    const int buf = t & (kBufs - 1);
+    // this wave's loads of tile t are done (those of tiles t + 1 and t + 2
+    // may still fly) ...
+    wait_all_but_last_tiles(wave, min(2, n_tiles - 1 - t));
     // ... and every wave's; every wave is also past tile t - 1, whose buffer
-    // tile t + 2 now takes
+    // tile t + 3 now takes
     __syncthreads();
-    if (t + 2 < n_tiles) copy_tile(t + 2, (t + 2) % kBufs);
+    if (t + 3 < n_tiles) copy_tile(t + 3, (t + 3) & (kBufs - 1));
     if (wave_live) {
       // the tile's base, stated 16-byte aligned so that the K operand reads
-      // stay single ds_read_b128 (the compiler loses it through t % 3)
+      // stay single ds_read_b128 (the compiler loses it through the buffer index)
       const uint16_t* tile = static_cast<const uint16_t*>(__builtin_assume_aligned(sm.kv[buf], 16));
       // S^T = K Q^T: keys 16 kb + 4 g + i of head col in sacc[kb][i]
       // the two key blocks' chains alternate; each k-step's operands are
