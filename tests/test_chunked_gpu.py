@@ -114,13 +114,15 @@ CHUNK_CASES = [
     (2, 4, 2, 128, 70, [130, 0], True, 16, True, 0),
     (2, 4, 2, 64, 128, [64, 200], True, 16, True, 0),
     (1, 8, 2, 128, 200, [333], True, 32, True, 0),
-    (2, 4, 1, 128, 65, [7, 100], True, 4, True, 0),        # block smaller than a wave's 16 rows
+    (2, 4, 1, 128, 65, [7, 100], True, 4, True, 0),        # block smaller than a wave's 8 copied rows
     (1, 4, 2, 64, 33, [90], True, 1, True, 0),
     (2, 4, 4, 128, 64, [256, 3], True, 128, True, 0),
     (3, 4, 2, 128, 50, [80, 96, 150], True, 16, True, 4),  # a shared 64-token prefix
     (2, 4, 2, 128, 70, [130, 0], False, 0, True, 0),       # contiguous cache
     (2, 8, 4, 64, 100, [20, 300], False, 0, True, 0),
     (2, 4, 2, 128, 40, [100, 10], True, 16, False, 0),     # every query sees the whole cache
+    (2, 4, 2, 128, 600, [100, 1000], True, 8, True, 0),    # three 256-row query tiles; blocks of a wave's 8 rows
+    (1, 4, 2, 64, 530, [70], True, 16, True, 0),           # three query tiles, d = 64
 ]
 
 

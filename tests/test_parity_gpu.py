@@ -68,6 +68,10 @@ PREFILL_CASES = [
     (1, 4, 2, 70, 200, 128, True),        # chunked prefill, bottom-right mask
     (1, 4, 2, 1, 333, 64, True),          # a single new query against a cache
     (1, 2, 2, 383, 383, 128, True),       # three query tiles, ragged
+    # the bf16 kernel runs query tiles of 256 rows in complementary pairs:
+    (1, 4, 2, 700, 700, 128, True),       # three tiles: a pair plus the lone middle one
+    (1, 2, 1, 1200, 1300, 64, True),      # five tiles, bottom-right mask, d = 64
+    (2, 2, 2, 520, 520, 128, False),      # three tiles, no mask
 ]
 
 
