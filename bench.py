@@ -17,7 +17,8 @@ plus q, o, lse and the block-table entries read).  Kernel durations come from
 HIP events recorded around each launch on the stream the kernels run on.
 ``extras`` (outside the step, skipped with --no-extras) times the KV append,
 the chunked prefill against a paged cache, sliding-window prefill and decode,
-decode against an FP8 cache and MLA decode, each on its own.
+decode against an FP8 cache, the long-context prefill (N = 32768) and decode
+against a contiguous cache, and MLA decode, each on its own.
 """
 from __future__ import annotations
 
@@ -81,9 +82,12 @@ def measured_traffic(kind: str):
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
-def time_launches(fn, steps: int, warmup: int):
+def time_launches(fn, steps: int, warmup: int, back_to_back: bool = False):
     """Average and median kernel time (ms) of fn() over `steps` launches, from
-    HIP events recorded around each launch on the current stream."""
+    HIP events recorded around each launch on the current stream.  With
+    back_to_back, also the average over `steps` launches issued between one
+    pair of events (for kernels of a few microseconds, where the per-launch
+    events' own cost shows)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -95,7 +99,15 @@ def time_launches(fn, steps: int, warmup: int):
         b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return sum(ms) / steps, ms[steps // 2]
+    if not back_to_back:
+        return sum(ms) / steps, ms[steps // 2]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return sum(ms) / steps, ms[steps // 2], a.elapsed_time(b) / steps
 
 
 def extras(dev, steps: int, dec):
@@ -126,7 +138,7 @@ def extras(dev, steps: int, dec):
                                 scale=w.scale, out=o, lse=lse)
 
     append()
-    a_avg, a_med = time_launches(append, steps, 20)
+    a_avg, a_med, a_b2b = time_launches(append, steps, 20, back_to_back=True)
     c_avg, c_med = time_launches(chunk, steps, 50)
     flops = w.flops(ci.seq_lens.tolist())
     # new K/V read and written once, plus seq_lens and the table entries of the written blocks
@@ -134,7 +146,9 @@ def extras(dev, steps: int, dec):
                for L in ci.seq_lens.tolist())
     abytes = w.append_bytes() + w.B * 4 + ents * 4
     tf = flops / (c_avg * 1e-3) / 1e12
-    gbs = abytes / (a_avg * 1e-3) / 1e9
+    # a ~10 us kernel: rated on back-to-back launches (the per-launch events'
+    # own cost is a sizeable part of each bracketed interval)
+    gbs = abytes / (a_b2b * 1e-3) / 1e9
     out.update({
         "chunked_prefill": {"workload": w.name, "value": round(tf, 3), "unit": "TFLOP/s",
                             "kernel_ms": round(c_avg, 5), "kernel_ms_median": round(c_med, 5), "flops": flops,
@@ -143,8 +157,9 @@ def extras(dev, steps: int, dec):
                                          "kernel": "prefill_bf16_kernel<128, paged, no window>"}},
         "kv_append": {"workload": f"append of the same chunks ({w.B} x {w.chunk} tokens, {w.Hkv} KV heads, "
                                   f"d={w.d}, bf16) into the paged pool",
-                      "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(a_avg, 5),
-                      "kernel_ms_median": round(a_med, 5), "bytes": abytes,
+                      "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(a_b2b, 5),
+                      "kernel_ms_per_launch_events": round(a_avg, 5), "kernel_ms_median": round(a_med, 5),
+                      "bytes": abytes,
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "kv_append_kernel"}},
     })
@@ -217,6 +232,42 @@ def extras(dev, steps: int, dec):
                                       "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                       "kernel": "decode_split_kernel<fp8,128,4,paged> + decode_merge_kernel"}}
     del fk, fv
+
+    # the two configurations of the hot path outside the step, each on its own:
+    # long-context causal GQA prefill (N = 32768, 64 query heads) ...
+    w4 = W.C4
+    q, k, v = (t.to(dev) for t in W.prefill_inputs(w4))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    p_avg, p_med = time_launches(lambda: binding.prefill(q, k, v, causal=True, scale=w4.scale, out=o, lse=lse),
+                                 max(5, steps // 5), 3)
+    tf = w4.flops() / (p_avg * 1e-3) / 1e12
+    out["prefill_long"] = {"workload": w4.name, "value": round(tf, 3), "unit": "TFLOP/s", "kernel_ms": round(p_avg, 5),
+                           "kernel_ms_median": round(p_med, 5), "flops": w4.flops(),
+                           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                        "kernel": "prefill_bf16_kernel<128, contiguous, no window>"}}
+    del q, k, v, o, lse
+    # ... and decode against a contiguous cache (64 sequences, S_cap 8192)
+    w3 = W.C3
+    di = W.decode_inputs(w3)
+    cq, ck, cv, cl = di.q.to(dev), di.k_cache.to(dev), di.v_cache.to(dev), di.seq_lens.to(dev)
+    st = binding.decode_split_tokens(w3.B, w3.Hq, w3.Hkv, w3.d, di.max_seq_len)
+    ws = torch.empty(max(1, binding.decode_workspace_bytes(w3.B, w3.Hq, w3.Hkv, w3.d, di.max_seq_len, st)),
+                     dtype=torch.uint8, device=dev)
+    co = torch.empty_like(cq)
+    cls = torch.empty(cq.shape[:2], dtype=torch.float32, device=dev)
+    d_avg, d_med = time_launches(lambda: binding.decode(cq, ck, cv, cl, max_seq_len=di.max_seq_len, scale=w3.scale,
+                                                        split_tokens=st, workspace=ws, out=co, lse=cls), steps, 20)
+    cbytes = di.kv_bytes() + cq.numel() * 2 * 2 + cls.numel() * 4 + w3.B * 4
+    gbs = cbytes / (d_avg * 1e-3) / 1e9
+    out["decode_contiguous"] = {"workload": w3.name, "value": round(gbs, 2), "unit": "GB/s",
+                                "kernel_ms": round(d_avg, 5), "kernel_ms_median": round(d_med, 5), "bytes": cbytes,
+                                "split_tokens": st,
+                                "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                             "kernel": "decode_split_kernel<bf16,128,4,contiguous> + decode_merge_kernel"}}
+    del cq, ck, cv, co, di
 
     # MLA decode (absorbed latent form), DeepSeek-V3-shaped batch
     wm = W.MLA_DECODE
