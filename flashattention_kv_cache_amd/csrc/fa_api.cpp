@@ -49,6 +49,10 @@ int choose_split_tokens(int B, int Hq, int Hkv, int max_seq_len) {
   const int n_rep = Hq / Hkv;
   const int qh = n_rep % 8 == 0 ? 8 : n_rep % 4 == 0 ? 4 : n_rep % 2 == 0 ? 2 : 1;
   const double pairs = (double)B * Hkv * (n_rep / qh);
+  // at least four workgroups per CU and short spans (a sliding window): one
+  // split per pair, no merge (measured on MI355X: 6.6% faster than 1024-token
+  // splits for 128 sequences x 8 KV heads with a 4096-token window)
+  if (pairs >= 1024 && max_seq_len <= 4096) return max(256, (max_seq_len + 255) / 256 * 256);
   const double want = pairs * (double)max_seq_len / 12288.0;
   // with few pairs, short splits are what fills the GPU
   const long long lo = pairs >= 256 ? 1024 : 256, step = want >= 1024 ? 512 : 256;
