@@ -387,7 +387,8 @@ size_t fa_mla_decode_workspace_bytes(int B, int Hq, int d_c, int d_r, int max_se
   const size_t slots = (size_t)B * Hq * ns;
   const size_t o_bytes = (slots * d_c * sizeof(float) + 255) & ~(size_t)255;
   const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
-  return o_bytes + l_bytes;
+  const size_t p_bytes = ((1 + (size_t)B * ns) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return o_bytes + l_bytes + p_bytes;
 }
 
 int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, const int32_t* block_table,
@@ -413,7 +414,7 @@ int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, 
       return fail(FA_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID, "workspace must be 256-byte aligned");
   }
-  if (B > 65535 || ns > 0x7fffffff || (Hq + 127) / 128 > 65535)
+  if (B > 65535 || (long long)B * ns >= 0x7fffffff || (Hq + 127) / 128 > 65535)
     return fail(FA_ERR_UNSUPPORTED, "grid too large (B <= 65535)");
 
   fa::MlaArgs a{};
@@ -427,8 +428,10 @@ int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, 
   if (ns > 1) {
     const size_t slots = (size_t)B * Hq * ns;
     const size_t o_bytes = (slots * d_c * sizeof(float) + 255) & ~(size_t)255;
+    const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = reinterpret_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+    a.plan = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + o_bytes + l_bytes);
   }
   hipError_t e = fa::launch_mla_decode(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

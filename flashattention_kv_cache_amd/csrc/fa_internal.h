@@ -80,6 +80,7 @@ struct MlaArgs {
   int split_tokens, max_splits;
   float* ws_o;                 // (B, Hq, max_splits, DC) partial outputs, when max_splits > 1
   float* ws_lse;               // (B, Hq, max_splits)
+  int32_t* plan;               // 1 + B * max_splits: count, then b * max_splits + s, longest first
 };
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
 

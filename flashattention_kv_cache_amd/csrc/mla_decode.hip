@@ -107,19 +107,77 @@ __device__ __forceinline__ void wait_all_but_last_tiles(int wave, int younger) {
   }
 }
 
+// With several splits, a sequence of L tokens is cut into ns = ceil(L /
+// split_tokens) equal parts of sl = ceil(L / ns) tokens, rounded up to a tile
+// (sl <= split_tokens, and every part is non-empty), and the work items
+// (sequence, part) are dispatched longest first from the list the plan
+// kernel writes: one workgroup per CU takes them as CUs free up.
+__device__ __forceinline__ int split_len(int L, int ns) {
+  return ns <= 1 ? L : ((L + ns - 1) / ns + kBN - 1) / kBN * kBN;
+}
+__device__ __forceinline__ int split_count(const MlaArgs& a, int L) {
+  const bool bad = L < 0 || L > a.max_seq_len;
+  return bad ? 1 : max(1, (L + a.split_tokens - 1) / a.split_tokens);
+}
+
+// One workgroup: the list of work items sorted by tile count, longest first
+// (a counting sort; the order among equal counts is free, and no result
+// depends on it).  plan[0] = number of items.
+constexpr int kPlanThreads = 256, kPlanBuckets = 1024;
+__global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(MlaArgs a) {
+  __shared__ int cnt[kPlanBuckets];
+  for (int i = threadIdx.x; i < kPlanBuckets; i += kPlanThreads) cnt[i] = 0;
+  __syncthreads();
+  auto bucket = [&](int L, int ns, int s) {
+    if (L < 0 || L > a.max_seq_len) return 0;
+    const int sl = split_len(L, ns), t0 = s * sl, t1 = min(L, t0 + sl);
+    return min(kPlanBuckets - 1, (t1 - t0 + kBN - 1) / kBN);
+  };
+  for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
+    const int L = a.seq_lens[b], ns = split_count(a, L);
+    for (int s = 0; s < ns; ++s) atomicAdd(&cnt[kPlanBuckets - 1 - bucket(L, ns, s)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive prefix sum, longest bucket first
+    int run = 0;
+    for (int i = 0; i < kPlanBuckets; ++i) {
+      const int c = cnt[i];
+      cnt[i] = run;
+      run += c;
+    }
+    a.plan[0] = run;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
+    const int L = a.seq_lens[b], ns = split_count(a, L);
+    for (int s = 0; s < ns; ++s) {
+      const int pos = atomicAdd(&cnt[kPlanBuckets - 1 - bucket(L, ns, s)], 1);
+      a.plan[1 + pos] = b * a.max_splits + s;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
   __shared__ Smem sm;
-  const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+  const int hg = blockIdx.z;
+  int s = 0, b = blockIdx.y;
+  if (a.plan) {  // several splits: the work item from the longest-first list
+    if ((int)blockIdx.x >= a.plan[0]) return;
+    const int item = a.plan[1 + blockIdx.x];
+    b = item / a.max_splits;
+    s = item % a.max_splits;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, col = lane & 15;
 
   const int L = a.seq_lens[b];
   bool bad = L < 0 || L > a.max_seq_len;
-  const int ns = bad ? 1 : max(1, (L + a.split_tokens - 1) / a.split_tokens);
+  const int ns = split_count(a, L);
   if (s >= ns) return;
-  const int t_begin = bad ? 0 : s * a.split_tokens;
-  const int t_end = bad ? 0 : min(L, t_begin + a.split_tokens);
+  const int sl = split_len(L, ns);
+  const int t_begin = bad ? 0 : s * sl;
+  const int t_end = bad ? 0 : min(L, t_begin + sl);
   const int n_tiles = (t_end - t_begin + kBN - 1) / kBN;
 
   const int h = hg * kHeadsWG + wave * kHeadsWave + col;  // this lane's head
@@ -409,8 +467,12 @@ __global__ __launch_bounds__(kDC / 4) void mla_merge_kernel(MlaArgs a) {
 
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
   const int hgroups = (a.Hq + kHeadsWG - 1) / kHeadsWG;
-  dim3 grid(a.max_splits, a.B, hgroups);
-  hipLaunchKernelGGL(mla_split_kernel, grid, dim3(kThreads), 0, st, a);
+  if (a.max_splits > 1) {
+    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+    hipLaunchKernelGGL(mla_split_kernel, dim3(a.B * a.max_splits, 1, hgroups), dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(mla_split_kernel, dim3(1, a.B, hgroups), dim3(kThreads), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL(mla_merge_kernel, dim3(a.B * a.Hq), dim3(kDC / 4), 0, st, a);

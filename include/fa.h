@@ -265,7 +265,9 @@ int fa_kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* 
  *   o            (B, Hq, d_c) bf16 output
  *   lse          (B, Hq) fp32 output or NULL
  *   split_tokens 0 = library choice (fa_mla_decode_split_tokens), else a
- *                multiple of 32
+ *                multiple of 32: a sequence of L tokens is cut into
+ *                ceil(L / split_tokens) parts of equal length (rounded up to
+ *                32 tokens), whose partials are merged
  *   workspace    fa_mla_decode_workspace_bytes(...) bytes (NULL if 0)
  *
  * Contract: d_c = 512 and d_r = 64 (the shape built); 0 <= L_b <= max_seq_len;
@@ -280,7 +282,9 @@ int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, 
 /* Tokens per split fa_mla_decode uses when called with split_tokens = 0 (0 for rejected sizes). */
 int fa_mla_decode_split_tokens(int B, int Hq, int d_c, int d_r, int max_seq_len);
 
-/* Workspace bytes fa_mla_decode needs (0 when every sequence fits in one split or the sizes are rejected). */
+/* Workspace bytes fa_mla_decode needs (0 when every sequence fits in one split or the sizes are rejected):
+ * the split partials (B x Hq x splits x d_c fp32, then their log-sum-exps) and a
+ * work list (1 + B x splits int32) that orders the splits longest first. */
 size_t fa_mla_decode_workspace_bytes(int B, int Hq, int d_c, int d_r, int max_seq_len, int split_tokens);
 
 /*

@@ -310,7 +310,8 @@ def test_mla_workspace_and_split_contract(fa):
     assert L.fa_mla_decode_workspace_bytes(2, 128, 512, 64, 256, 256) == 0
     n = L.fa_mla_decode_workspace_bytes(2, 128, 512, 64, 1024, 256)
     slots = 2 * 128 * 4
-    assert n == ((slots * 512 * 4 + 255) // 256) * 256 + ((slots * 4 + 255) // 256) * 256
+    plan = (1 + 2 * 4) * 4  # item count, then one entry per (sequence, split)
+    assert n == sum((x + 255) // 256 * 256 for x in (slots * 512 * 4, slots * 4, plan))
     assert L.fa_mla_decode_workspace_bytes(2, 128, 256, 64, 1024, 256) == 0
     st = L.fa_mla_decode_split_tokens(128, 128, 512, 64, 16384)
     assert st >= 1024 and st % 256 == 0
