@@ -124,3 +124,57 @@ def test_mla_decode_full_size(fa):
     idx = tuple(torch.tensor(c) for c in zip(*heads))
     check(o.cpu()[idx], lse.cpu()[idx], O_ref[idx], lse_ref[idx], "mla full size")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def _expected_items(lens, max_seq_len, st):
+    """(item id, tile count) of every split the work list must hold: a valid
+    length L gives ceil(L / st) parts of equal length rounded up to 32 tokens,
+    an invalid one a single (NaN-flagging) item; ids are b * max_splits + s."""
+    ns_max = 1 if max_seq_len <= st else -(-max_seq_len // st)
+    items = {}
+    for b, L in enumerate(lens):
+        bad = L < 0 or L > max_seq_len
+        ns = 1 if bad else max(1, -(-L // st))
+        sl = L if ns <= 1 else -(-(-(-L // ns)) // 32) * 32
+        for s in range(ns):
+            t0 = s * sl
+            t1 = min(L, t0 + sl)
+            items[b * ns_max + s] = 0 if bad else min(1023, -(-(t1 - t0) // 32))
+    return items, ns_max
+
+
+@pytest.mark.parametrize("st", [4096, 24576])
+def test_mla_work_list_orders_every_split_longest_first(fa, st):
+    # Many sequences over a tiny pool (block ids repeat), so that lengths up to
+    # 40000 tokens cost little memory and the tile counts spread over most of
+    # the sort's buckets.
+    B, Hq, bs, nblk, max_len = 300, 16, 64, 32, 40000
+    g = torch.Generator().manual_seed(1300 + st)
+    lens = torch.randint(0, max_len + 1, (B,), generator=g, dtype=torch.int32)
+    lens[:4] = torch.tensor([0, 1, max_len, -1], dtype=torch.int32)
+    max_blocks = -(-max_len // bs)
+    table = torch.randint(0, nblk, (B, max_blocks), generator=g, dtype=torch.int32)
+    q = torch.randn((B, Hq, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((nblk, bs, 576), generator=g).to(torch.bfloat16)
+    note(f"mla work list B={B} st={st}")
+    need = fa.mla_decode_workspace_bytes(B, Hq, max_len, st)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    o, lse = fa.mla_decode(q.to(DEV), kv.to(DEV), lens.to(DEV), SCALE, block_table=table.to(DEV), max_seq_len=max_len,
+                           split_tokens=st, workspace=ws)
+    torch.cuda.synchronize()
+    items, ns = _expected_items(lens.tolist(), max_len, st)
+    slots = B * Hq * ns
+    off = -(-slots * 512 * 4 // 256) * 256 + -(-slots * 4 // 256) * 256
+    plan = ws[off:off + 4 * (1 + len(items))].cpu().view(torch.int32).tolist()
+    assert plan[0] == len(items)
+    order = plan[1:]
+    assert sorted(order) == sorted(items)
+    tiles = [items[i] for i in order]
+    assert all(x >= y for x, y in zip(tiles, tiles[1:])), "work list not longest first"
+    lse_h = lse.cpu()
+    assert torch.isnan(lse_h[3]).all() and torch.isfinite(lse_h[4:]).all()
+    # two sampled sequences against the oracle (paged reads through the repeated block ids)
+    for b in (2, 5):
+        L = int(lens[b])
+        O_ref, lse_ref = M.mla_decode_latent(q[b:b + 1], kv, lens[b:b + 1], SCALE, 512, table[b:b + 1], bs)
+        check(o[b:b + 1], lse[b:b + 1], O_ref, lse_ref, f"work list seq {b} L={L}")
