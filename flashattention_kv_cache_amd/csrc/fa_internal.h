@@ -134,6 +134,14 @@ __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950).  Unlike fmaxf it
+// needs no canonicalising v_max of each operand in IEEE mode; a NaN score
+// makes its row NaN either way.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float halves_max_nan(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);

@@ -424,14 +424,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       if (t >= n_clean || t < n_lo) mask(sc, t);
       float mx = sc[0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+      for (int r = 1; r < 16; ++r) mx = max_nan(mx, sc[0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-      mx = halves_max(mx) * c;
+      for (int r = 0; r < 16; ++r) mx = max_nan(mx, sc[1][r]);
+      mx = halves_max_nan(mx) * c;
       // Rescale only when some row's max grows by more than kSlack (log2
       // units): (m, l, O) stays exact for any reference m within kSlack of the
       // true max, and P is then at most 2^kSlack (fine in bf16).
-      const float mn = fmaxf(m, mx);
+      const float mn = max_nan(m, mx);
       if (__any(mn > m + kSlack)) {
         pend_alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
         pending = true;
