@@ -83,12 +83,14 @@ __device__ __forceinline__ void mfma_done(f32x4 (&acc)[2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
 }
 __device__ __forceinline__ void valu_done(bf16x8_t& p) { asm volatile("s_nop 3" : "+v"(p)); }
-// Orders an LDS operand read after the MFMA issued before it (an empty
-// statement that claims to change the read's element offset; the pointer
-// itself must keep its LDS address space).
-__device__ __forceinline__ int after_prev(int off) {
-  asm volatile("" : "+v"(off));
-  return off;
+// Orders an LDS operand read after the MFMA issued before it: an empty
+// statement that claims to change the read's base address in place (no copy,
+// no arithmetic), so the read cannot move above it, and the read's own offset
+// stays an immediate.
+__device__ __forceinline__ void after_prev(uint32_t& addr) { asm volatile("" : "+v"(addr)); }
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+__device__ __forceinline__ const lds_bf16x8* lds_ptr(uint32_t addr) {
+  return reinterpret_cast<const lds_bf16x8*>((uintptr_t)addr);
 }
 
 // Waves issue the 36 direct loads of a tile round-robin: wave w takes loads
@@ -335,15 +337,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
     __syncthreads();
     if (t + 3 < n_tiles) copy_tile(t + 3, (t + 3) & (kBufs - 1));
     if (wave_live) {
-      // the tile's base, stated 16-byte aligned so that the K operand reads
-      // stay single ds_read_b128 (the compiler loses it through the buffer index)
-      const uint16_t* tile = static_cast<const uint16_t*>(__builtin_assume_aligned(sm.kv[buf], 16));
+      // LDS byte addresses of this lane's operands in the tile's buffer; each
+      // read adds a constant as its immediate offset
+      const uint32_t tile = lds_of(buf);
       // S^T = K Q^T: keys 16 kb + 4 g + i of head col in sacc[kb][i]
       // the two key blocks' chains alternate; each k-step's operands are
       // read while the previous step's MFMAs run
+      uint32_t kaddr[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) kaddr[kb][par] = tile + 2 * kbase[kb][par];
       auto k_operand = [&](int kb, int ks) {
-        const uint16_t* p = tile + after_prev(kbase[kb][ks & 1] + 64 * (ks >> 1));
-        return *static_cast<const bf16x8_t*>(__builtin_assume_aligned(p, 16));
+        after_prev(kaddr[kb][ks & 1]);
+        return *lds_ptr(kaddr[kb][ks & 1] + 128 * (ks >> 1));
       };
       f32x4 sacc[2];
       bf16x8_t ka0 = k_operand(0, 0), ka1 = k_operand(1, 0);
@@ -400,13 +407,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
       valu_done(pc);
       // O^T += V^T P^T, one k-step of 32 keys per 16-dim block; each block's
       // operand is read while the previous block's MFMA runs
-      int vbase[4];
+      uint32_t vaddr[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vbase[q] = v_base(q);
+      for (int q = 0; q < 4; ++q) vaddr[q] = tile + 2 * v_base(q);
       auto v_operand = [&](int db) {
-        const uint16_t* p = tile + after_prev(vbase[db & 3] + 64 * (db >> 2));
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * kDK));
+        after_prev(vaddr[db & 3]);
+        const uint32_t p = vaddr[db & 3] + 128 * (db >> 2);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)p);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(p + 2 * 16 * kDK));
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8_t va = v_operand(0);
