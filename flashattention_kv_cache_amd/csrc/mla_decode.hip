@@ -246,11 +246,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
   }
   auto lds_of = [&](int buf) { return (uint32_t)(uintptr_t)(const lds_u16*)sm.kv[buf]; };
   auto entry = [&](int tok) { return sm.ent[(min(tok, t_end - 1) >> lbs) - e_lo]; };
+  // Byte offset, within its block's rows, of the unit this lane fetches in
+  // each of the wave's loads of a whole tile (the tile's rows 16-31 start a
+  // second block when block_size is 16).
+  constexpr int kLoadsWave = (kInstr + kWaves - 1) / kWaves;
+  uint32_t dma_off[kLoadsWave];
+#pragma unroll
+  for (int k = 0; k < kLoadsWave; ++k) {
+    const int i = min(wave + kWaves * k, kInstr - 1);
+    const int u = 64 * i + lane, r = u / kUnits, p = u - r * kUnits;
+    const int half = trow && bs == 16 ? i / (kInstr / 2) : 0;
+    dma_off[k] = (uint32_t)(((r - 16 * half) * kDK + (p ^ swz(r)) * 8) * 2);
+  }
   auto copy_tile = [&](int t, int buf) {
     const int tok0 = t_begin + t * kBN;
     const uint32_t lds0 = lds_of(buf);
-    // The per-lane unit arithmetic below is cheap; recomputing it per tile
-    // (the empty asm hides that it is loop-invariant) keeps ~15 registers free.
+    // The per-lane unit arithmetic of the partial-tile path below is cheap;
+    // recomputing it per tile (the empty asm hides that it is loop-invariant)
+    // keeps registers free.
     int ln = lane;
     asm volatile("" : "+v"(ln));
     if (blocky && tok0 + kBN <= t_end) {
@@ -263,18 +276,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
       for (int k = 0; k < (kInstr + kWaves - 1) / kWaves; ++k) {
         const int i = wave + kWaves * k;
         if (i >= kInstr) break;
-        const int u = 64 * i + ln, r = u / kUnits, p = u - r * kUnits;
-        const int lu = p ^ swz(r);
         const uint16_t* base;
-        int rr = r;
         if (trow) {
           const int half = bs == 16 ? i / (kInstr / 2) : 0;  // which block of the tile
-          rr = r - 16 * half;
           base = kv + ((size_t)(half ? e1 : e0) * bs + ((tok0 + 16 * half) & (bs - 1))) * kDK;
         } else {
           base = kv + ((size_t)b * a.kv_capacity + tok0) * kDK;
         }
-        lds_dma_saddr((uint32_t)((rr * kDK + lu * 8) * 2), base, lds0 + i * 1024);
+        lds_dma_saddr(dma_off[k], base, lds0 + i * 1024);
       }
     } else {
       // each lane finds its own token; rows past the split read its last
@@ -406,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
       bf16x8_t pc = __builtin_bit_cast(bf16x8_t, w);
       valu_done(pc);
       // O^T += V^T P^T, one k-step of 32 keys per 16-dim block; each block's
-      // operand is read while the previous block's MFMA runs
+      // operand is read while the two blocks before it run
       uint32_t vaddr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) vaddr[q] = tile + 2 * v_base(q);
@@ -417,13 +426,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(p + 2 * 16 * kDK));
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8_t va = v_operand(0);
+      bf16x8_t vq[3];  // operands of blocks db, db + 1 (read) and db + 2 (being read)
+      vq[0] = v_operand(0);
+      vq[1] = v_operand(1);
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        bf16x8_t vn = va;
-        if (db + 1 < kDB) vn = v_operand(db + 1);
-        mfma_acc(oacc[db], va, pc);
-        va = vn;
+        if (db + 2 < kDB) vq[(db + 2) % 3] = v_operand(db + 2);
+        mfma_acc(oacc[db], vq[db % 3], pc);
       }
     }
   }
