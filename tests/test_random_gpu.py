@@ -1,0 +1,167 @@
+"""Parity with the fp64 oracle on seeded random shapes, through the C ABI.
+
+The hand-picked cases in the other parity files cover the known edges; these
+draw head counts, GQA ratios, lengths, block sizes, split sizes, windows and
+dtypes from a fixed seed, so that combinations nobody picked are exercised
+too.  Every case is deterministic and named by its shape.  Tolerances as for
+every attention output: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and mean-abs
+2e-3; LSE 1e-4 (rows with no visible key: O = 0 and LSE = -inf on both
+sides).
+"""
+import math
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max=1e-5, mean=1e-5), "bf16": dict(max=2e-2, mean=2e-3)}
+LSE_TOL = 1e-4
+DEV = "cuda"
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(o_gpu, lse_gpu, O_ref, lse_ref, dt, what):
+    O = o_gpu.detach().to("cpu", torch.float64).numpy()
+    O_ref = np.asarray(O_ref)
+    assert O.shape == O_ref.shape, (what, O.shape, O_ref.shape)
+    assert np.isfinite(O).all(), f"{what}: non-finite output"
+    err = np.abs(O - O_ref)
+    assert err.max() <= TOL[dt]["max"], f"{what}: max abs err {err.max():.3e}"
+    assert err.mean() <= TOL[dt]["mean"], f"{what}: mean abs err {err.mean():.3e}"
+    L = lse_gpu.detach().to("cpu", torch.float64).numpy()
+    inf_ref = np.isneginf(lse_ref)
+    assert (np.isneginf(L) == inf_ref).all(), f"{what}: -inf LSE rows differ"
+    if (~inf_ref).any():
+        e = np.abs(L[~inf_ref] - lse_ref[~inf_ref]).max()
+        assert e <= LSE_TOL, f"{what}: LSE err {e:.3e}"
+
+
+def _heads(r):
+    hkv = r.choice([1, 1, 2, 2, 4, 8])
+    rep = r.choice([1, 2, 3, 4, 8])
+    while hkv * rep > 16:
+        rep = max(1, rep // 2)
+    return hkv * rep, hkv
+
+
+def _prefill_cases(n, seed):
+    r = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        hq, hkv = _heads(r)
+        d = r.choice([64, 128])
+        dt = "f32" if r.random() < 0.2 else "bf16"
+        causal = r.random() < 0.7
+        nk = r.randint(1, 600)
+        nq = r.randint(1, nk) if causal else r.randint(1, 600)
+        win = r.randint(1, nk) if causal and r.random() < 0.35 else 0
+        cases.append((r.choice([1, 2]), hq, hkv, nq, nk, d, causal, win, dt))
+    return cases
+
+
+def _decode_cases(n, seed):
+    r = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        hq, hkv = _heads(r)
+        d = r.choice([64, 128])
+        dt = "f32" if r.random() < 0.2 else "bf16"
+        B = r.randint(1, 5)
+        lens = [r.choice([0, r.randint(1, 64), r.randint(1, 1500)]) for _ in range(B)]
+        paged = r.random() < 0.6
+        bs = r.choice([1, 2, 4, 8, 16, 16, 32, 64, 128]) if paged else 0
+        split = r.choice([0, 0, 256, 512, 768, 2048])
+        win = r.randint(1, max(lens) + 5) if r.random() < 0.3 else 0
+        cases.append((B, hq, hkv, d, tuple(lens), paged, bs, split, win, dt))
+    return cases
+
+
+def _chunk_cases(n, seed):
+    r = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        hq, hkv = _heads(r)
+        d = r.choice([64, 128])
+        dt = "f32" if r.random() < 0.2 else "bf16"
+        B = r.randint(1, 3)
+        nq = r.randint(1, 400)
+        causal = r.random() < 0.8
+        lens = [nq + r.randint(0, 700) for _ in range(B)]
+        paged = r.random() < 0.7
+        bs = r.choice([1, 4, 8, 16, 32, 64]) if paged else 0
+        win = r.randint(1, max(lens)) if causal and r.random() < 0.3 else 0
+        cases.append((B, hq, hkv, d, nq, tuple(lens), paged, bs, causal, win, dt))
+    return cases
+
+
+PREFILL = _prefill_cases(24, 20261)
+DECODE = _decode_cases(24, 20262)
+CHUNKED = _chunk_cases(16, 20263)
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_d{}_{}_w{}_{}".format(
+    *c[:6], "causal" if c[6] else "full", c[7], c[8]))
+def test_random_prefill(fa, case):
+    B, Hq, Hkv, Nq, Nk, d, causal, win, dt = case
+    note(f"random prefill {case}")
+    q, k, v = W.make_prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dt, seed=Nq * 7 + Nk + d)
+    scale = 1 / math.sqrt(d)
+    O_ref, lse_ref = oracle.prefill(q, k, v, scale, causal, window=win)
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, window=win)
+    torch.cuda.synchronize()
+    check(o, lse, O_ref, lse_ref, dt, str(case))
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "B{}_Hq{}_Hkv{}_d{}_{}_{}_bs{}_st{}_w{}_{}".format(
+    c[0], c[1], c[2], c[3], "-".join(map(str, c[4])), "paged" if c[5] else "contig", *c[6:]))
+def test_random_decode(fa, case):
+    B, Hq, Hkv, d, lens, paged, bs, split, win, dt = case
+    note(f"random decode {case}")
+    di = W.make_decode_inputs(B, Hq, Hkv, d, dt, seed=sum(lens) % 991 + d, seq_lens=list(lens), paged=paged,
+                              block_size=bs or 16, s_cap=max(max(lens), 1) + 3, spare_blocks=2 if paged else 0)
+    scale = 1 / math.sqrt(d)
+    if paged:
+        O_ref, lse_ref = oracle.decode_paged(di.q, di.k_cache, di.v_cache, di.block_table, di.seq_lens, di.block_size,
+                                             scale, window=win)
+        o, lse = fa.decode(di.q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.seq_lens.to(DEV),
+                           block_table=di.block_table.to(DEV), max_seq_len=di.max_seq_len, split_tokens=split,
+                           window=win)
+    else:
+        O_ref, lse_ref = oracle.decode_contiguous(di.q, di.k_cache, di.v_cache, di.seq_lens, scale, window=win)
+        o, lse = fa.decode(di.q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.seq_lens.to(DEV),
+                           max_seq_len=di.max_seq_len, split_tokens=split, window=win)
+    torch.cuda.synchronize()
+    check(o, lse, O_ref, lse_ref, dt, str(case))
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=lambda c: "B{}_Hq{}_Hkv{}_d{}_n{}_{}_{}_bs{}_{}_w{}_{}".format(
+    c[0], c[1], c[2], c[3], c[4], "-".join(map(str, c[5])), "paged" if c[6] else "contig", c[7],
+    "causal" if c[8] else "full", c[9], c[10]))
+def test_random_chunked_prefill(fa, case):
+    """The Nq newest tokens of each sequence against its whole cache, the cache
+    written beforehand (its lengths count the new tokens)."""
+    B, Hq, Hkv, d, nq, lens, paged, bs, causal, win, dt = case
+    note(f"random chunked prefill {case}")
+    di = W.make_decode_inputs(B, Hq, Hkv, d, dt, seed=sum(lens) % 983 + nq, seq_lens=list(lens), paged=paged,
+                              block_size=bs or 16, s_cap=max(lens) + 5, spare_blocks=2 if paged else 0)
+    q, _, _ = W.make_prefill_inputs(B, Hq, 1, nq, 1, d, dt, seed=nq + d)
+    scale = 1 / math.sqrt(d)
+    table = di.block_table if paged else None
+    O_ref, lse_ref = oracle.chunked_prefill(q, di.k_cache, di.v_cache, di.seq_lens, scale, causal,
+                                            table, di.block_size if paged else 0, window=win)
+    o, lse = fa.chunked_prefill(q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.seq_lens.to(DEV),
+                                block_table=table.to(DEV) if paged else None, max_seq_len=di.max_seq_len,
+                                causal=causal, scale=scale, window=win)
+    torch.cuda.synchronize()
+    check(o, lse, O_ref, lse_ref, dt, str(case))
