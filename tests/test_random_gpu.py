@@ -17,6 +17,8 @@ import pytest
 import torch
 
 import oracle
+from oracle import fp8 as F
+from oracle import mla as M
 from flashattention_kv_cache_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -105,9 +107,25 @@ def _chunk_cases(n, seed):
     return cases
 
 
+def _mla_cases(n, seed):
+    r = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        B = r.randint(1, 4)
+        Hq = r.choice([8, 16, 40, 64, 128, 144])
+        lens = [r.choice([0, r.randint(1, 100), r.randint(1, 3000)]) for _ in range(B)]
+        paged = r.random() < 0.7
+        bs = r.choice([1, 4, 8, 16, 32, 64]) if paged else 0
+        split = r.choice([0, 0, 32, 256, 640, 2048])
+        cases.append((B, Hq, tuple(lens), paged, bs, split))
+    return cases
+
+
 PREFILL = _prefill_cases(24, 20261)
 DECODE = _decode_cases(24, 20262)
 CHUNKED = _chunk_cases(16, 20263)
+FP8 = [c for c in _decode_cases(12, 20264)]
+MLA = _mla_cases(16, 20265)
 
 
 @pytest.mark.parametrize("case", PREFILL, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_d{}_{}_w{}_{}".format(
@@ -165,3 +183,42 @@ def test_random_chunked_prefill(fa, case):
                                 causal=causal, scale=scale, window=win)
     torch.cuda.synchronize()
     check(o, lse, O_ref, lse_ref, dt, str(case))
+
+
+@pytest.mark.parametrize("case", FP8, ids=lambda c: "B{}_Hq{}_Hkv{}_d{}_{}_{}_bs{}_st{}_w{}".format(
+    c[0], c[1], c[2], c[3], "-".join(map(str, c[4])), "paged" if c[5] else "contig", *c[6:9]))
+def test_random_fp8_decode(fa, case):
+    """bf16 queries against an E4M3 cache (per-tensor scales)."""
+    B, Hq, Hkv, d, lens, paged, bs, split, win, _ = case
+    note(f"random fp8 decode {case}")
+    di = W.make_decode_inputs(B, Hq, Hkv, d, "fp8", seed=sum(lens) % 977 + d, seq_lens=list(lens), paged=paged,
+                              block_size=bs or 16, s_cap=max(max(lens), 1) + 3, spare_blocks=2 if paged else 0)
+    scale = 1 / math.sqrt(d)
+    ks, vs = W.FP8_SCALE, W.FP8_SCALE * 0.75
+    table = di.block_table if paged else None
+    O_ref, lse_ref = F.decode_fp8(di.q, di.k_cache, di.v_cache, di.seq_lens, scale, ks, vs, table, di.block_size,
+                                  window=win)
+    o, lse = fa.decode_fp8(di.q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.seq_lens.to(DEV), ks, vs,
+                           block_table=table.to(DEV) if paged else None, max_seq_len=di.max_seq_len, scale=scale,
+                           split_tokens=split, window=win)
+    torch.cuda.synchronize()
+    check(o, lse, O_ref, lse_ref, "bf16", str(case))
+
+
+@pytest.mark.parametrize("case", MLA, ids=lambda c: "B{}_Hq{}_{}_{}_bs{}_st{}".format(
+    c[0], c[1], "-".join(map(str, c[2])), "paged" if c[3] else "contig", c[4], c[5]))
+def test_random_mla_decode(fa, case):
+    """Absorbed-latent MLA decode (d_c = 512, d_r = 64) in latent space."""
+    B, Hq, lens, paged, bs, split = case
+    note(f"random mla decode {case}")
+    mi = W.make_mla_inputs(B, Hq, 512, 64, sum(lens) % 971 + Hq, seq_lens=list(lens), paged=paged,
+                           block_size=bs or 16, s_cap=None if paged else max(max(lens), 1) + 7,
+                           spare_blocks=1 if paged else 0)
+    scale = 1 / math.sqrt(128 + 64)
+    table = mi.block_table if paged else None
+    O_ref, lse_ref = M.mla_decode_latent(mi.q, mi.kv, mi.seq_lens, scale, 512, table, mi.block_size)
+    o, lse = fa.mla_decode(mi.q.to(DEV), mi.kv.to(DEV), mi.seq_lens.to(DEV), scale,
+                           block_table=table.to(DEV) if paged else None, max_seq_len=mi.max_seq_len,
+                           split_tokens=split)
+    torch.cuda.synchronize()
+    check(o, lse, O_ref, lse_ref, "bf16", str(case))
