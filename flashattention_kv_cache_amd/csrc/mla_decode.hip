@@ -29,9 +29,9 @@
 //     the transposed V reads (8 rows x 2 units) free of conflicts at this
 //     1152-byte row stride, where other XOR patterns conflict 2- to 4-way;
 //   * four tile buffers: tiles t + 1 .. t + 3 load while tile t is computed
-//     (three tiles in flight per CU, what HBM latency asks for here), one
-//     barrier per tile; a split's block ids are staged in LDS first, so no
-//     vector-memory wait of the loop can stall on tile loads in flight;
+//     (three tiles in flight per CU), one barrier per tile; a split's block
+//     ids are staged in LDS first, so no vector-memory wait of the loop can
+//     stall on tile loads in flight;
 //   * the S^T accumulator gives a lane keys 4 g + i and 16 + 4 g + i (g = lane
 //     / 16) of its head: packed in that order they are the B operand of PV as
 //     they stand, and the transposed V reads fetch the same key rows;
