@@ -464,12 +464,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
           l1 += p1;
           w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
         }
-        // interleave: next group's LDS reads, then each MFMA followed by half
-        // of the vector work
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        // interleave: each MFMA, then some of the next group's LDS reads (K
+        // and the first V^T half after the first, the second V^T half after
+        // the second), then half of the vector work
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // VALU incl. transcendental
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
       }
 #pragma unroll
