@@ -67,9 +67,15 @@ constexpr float kSlack = 8.f;  // log2 units a running max may lag before rescal
 
 template <int D>
 struct Smem {
-  uint16_t k[2][kBN * D];  // row-major K tiles, chunks swizzled by row % 8
-  uint16_t v[2][kBN * D];  // row-major V tiles, chunks swizzled by 2 * (row % 4)
+  union {
+    struct {
+      uint16_t k[2][kBN * D];  // row-major K tiles, chunks swizzled by row % 8
+      uint16_t v[2][kBN * D];  // row-major V tiles, chunks swizzled by 2 * (row % 4)
+    };
+    uint16_t o[kWaves][32 * D];  // epilogue: each wave's 32 output rows, chunks swizzled as K
+  };
 };
+static_assert(sizeof(Smem<128>) == 4 * kBN * 128 * 2 && sizeof(Smem<64>) == 4 * kBN * 64 * 2, "O staging fits the K/V tiles");
 
 // The LDS has 64 banks of 4 bytes: a 16-byte read is served 16 lanes per
 // cycle, an 8-byte read 32 lanes per cycle.  Swizzles are XOR masks on the
@@ -526,24 +532,41 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       else pv(p_a, (t - 1) & 1);
     }
 
-    // ---- epilogue: one division, bf16 output, natural-log LSE
+    // ---- epilogue: one division, bf16 output, natural-log LSE.  O leaves
+    // through LDS: each wave writes its 32 rows there as the accumulator holds
+    // them (lane: one row, 8 bytes of a chunk) and reads them back whole-row
+    // (lane: one 16-byte chunk), so that each global store covers 1 KiB of
+    // consecutive rows instead of 16 bytes of 32 rows.  Chunk c of row r sits
+    // at c ^ k_swz(r), which keeps both the writes and the reads free of bank
+    // conflicts.
     const float lt = halves_sum(l0 + l1);
-    if (qrow < a.Nq) {
-      const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qrow) * D;
+    const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
+    __syncthreads();  // every wave's last PV has read its V tile
+    // The lane's row and lane index pass through an empty statement, so that
+    // the swizzled addresses below are formed here and not kept in registers
+    // across the tile loop.
+    int ecol = col, elane = lane;
+    asm volatile("" : "+v"(ecol), "+v"(elane));
+    uint16_t* ot = sm.o[wave];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = db * 32 + q4 * 8 + hl * 4;
-          u32x2_t w;
-          w[0] = pack_bf16x2(oacc[db][q4 * 4 + 0] * inv, oacc[db][q4 * 4 + 1] * inv);
-          w[1] = pack_bf16x2(oacc[db][q4 * 4 + 2] * inv, oacc[db][q4 * 4 + 3] * inv);
-          *reinterpret_cast<u32x2_t*>(op + d) = w;
-        }
-      if (a.lse && hl == 0)
-        a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2_t w;
+        w[0] = pack_bf16x2(oacc[db][q4 * 4 + 0] * inv, oacc[db][q4 * 4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][q4 * 4 + 2] * inv, oacc[db][q4 * 4 + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(ot + ecol * D + (((db * 4 + q4) ^ k_swz<D>(ecol)) * 8) + hl * 4) = w;
+      }
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + q0 + wave * 32) * D;
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int u = i * 64 + elane, r = u / CPR, ch = u % CPR;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + r * D + ((ch ^ k_swz<D>(r)) * 8));
+      if (q0 + wave * 32 + r < a.Nq) *reinterpret_cast<u32x4_t*>(obase + r * D + ch * 8) = val;
     }
+    if (a.lse && hl == 0 && qrow < a.Nq)
+      a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
   };
   run_tile(nqb - 1 - pr);
   if (pr < nqb - 1 - pr) {
