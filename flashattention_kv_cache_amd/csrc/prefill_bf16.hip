@@ -537,9 +537,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // them (lane: one row, 8 bytes of a chunk) and reads them back whole-row
     // (lane: one 16-byte chunk), so that each global store covers 1 KiB of
     // consecutive rows instead of 16 bytes of 32 rows.  Chunk c of row r sits
-    // at c ^ k_swz(r), and rows 16-31 keep the two 8-byte halves of a chunk
-    // swapped, so that the 32 rows a half-wave writes land in 32 different
-    // bank pairs and the whole-chunk reads stay conflict-free.
+    // at c ^ k_swz(r), which keeps both the writes and the reads free of bank
+    // conflicts.
     const float lt = halves_sum(l0 + l1);
     const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
     __syncthreads();  // every wave's last PV has read its V tile
@@ -556,15 +555,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         u32x2_t w;
         w[0] = pack_bf16x2(oacc[db][q4 * 4 + 0] * inv, oacc[db][q4 * 4 + 1] * inv);
         w[1] = pack_bf16x2(oacc[db][q4 * 4 + 2] * inv, oacc[db][q4 * 4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(ot + ecol * D + (((db * 4 + q4) ^ k_swz<D>(ecol)) * 8) + ((hl ^ (ecol >> 4)) & 1) * 4) = w;
+        *reinterpret_cast<u32x2_t*>(ot + ecol * D + (((db * 4 + q4) ^ k_swz<D>(ecol)) * 8) + hl * 4) = w;
       }
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + q0 + wave * 32) * D;
 #pragma unroll
     for (int i = 0; i < 32 * CPR / 64; ++i) {
       const int u = i * 64 + elane, r = u / CPR, ch = u % CPR;
-      u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + r * D + ((ch ^ k_swz<D>(r)) * 8));
-      if (i >= 16 * CPR / 64) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);  // rows 16-31: halves swapped
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + r * D + ((ch ^ k_swz<D>(r)) * 8));
       if (q0 + wave * 32 + r < a.Nq) *reinterpret_cast<u32x4_t*>(obase + r * D + ch * 8) = val;
     }
     if (a.lse && hl == 0 && qrow < a.Nq)
