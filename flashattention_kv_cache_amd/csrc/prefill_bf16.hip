@@ -537,8 +537,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // them (lane: one row, 8 bytes of a chunk) and reads them back whole-row
     // (lane: one 16-byte chunk), so that each global store covers 1 KiB of
     // consecutive rows instead of 16 bytes of 32 rows.  Chunk c of row r sits
-    // at c ^ k_swz(r), which keeps both the writes and the reads free of bank
-    // conflicts.
+    // at c ^ k_swz(r): the whole-chunk reads are conflict-free, and the 8-byte
+    // writes cost the LDS about 64 conflict cycles per wave and tile (1.4% of
+    // its active cycles, measured).
     const float lt = halves_sum(l0 + l1);
     const float inv = bad ? __builtin_nanf("") : lt > 0.f ? 1.f / lt : 0.f;
     __syncthreads();  // every wave's last PV has read its V tile
