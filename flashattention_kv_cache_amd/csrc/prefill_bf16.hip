@@ -264,6 +264,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // tiles in [n_lo, n_clean) need no mask for any row of the workgroup
     const int n_clean = a.causal ? min((q0 + off + 1) / kBN, Nk / kBN) : Nk / kBN;
     const int n_lo = W > 0 ? (max(0, last_row + off - W + 1) + kBN - 1) / kBN : 0;
+    // causal: tiles [tb, te_w) hold a key that some row of this wave sees
+    const int te_w = a.causal ? min(te, max(tb, (min(q0 + wave * 32 + 31, a.Nq - 1) + off) / kBN + 1)) : te;
 
     // ---- Q^T operand fragments, kept in registers
     const int qrow = q0 + wave * 32 + col;
@@ -389,9 +391,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // on the vector ALUs, while the matrix cores run QK^T of tile t+1 (into sn)
     // and PV of tile t-1 (weights pp, V in buffer (t-1)&1).  The direct loads
     // of K(t+2) and V(t) fly during the whole stage.
-    auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
-                     bool with_pv) {
-      const int kb_next = (t + 1) & 1;  // K(t+1)
+    // The start of stage t: the direct loads of K(t+2) and V(t), then the
+    // rescale decided in the previous stage, which applies to O once PV(t-2)
+    // (its weights used the old reference) is in, i.e. now, before PV(t-1).
+    auto stage_start = [&](int t) {
       if (t + 2 < te) copy_k(sm.k[t & 1], t + 2, eK);
       copy_v(sm.v[t & 1], t, eV);
       if (PAGED && one_block) {
@@ -399,9 +402,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         eV = entry(t + 1);
         asm volatile("" ::: "memory");  // the lookups fly during this stage
       }
-
-      // A rescale decided in the previous stage applies to O once PV(t-2) (its
-      // weights used the old reference) is in, i.e. now, before PV(t-1) starts.
       if (pending) {
 #pragma unroll
         for (int i = 0; i < DB; ++i)
@@ -409,24 +409,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
           for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
         pending = false;
       }
-
-      // Operands of group j of the interleave below (QK^T k-step j % KS of
-      // key block j / KS, and PV MFMA j), read from LDS one group ahead of
-      // their MFMAs so that no MFMA waits for an LDS read it just issued.
-      auto k_operand = [&](int j) {
-        return *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(j / KS, j % KS)]);
-      };
-      auto v_operand = [&](int j) {
-        const int kk = j / DB, db = j % DB;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
-        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8_t ka_n = k_operand(0), va_n{};
-      if (with_pv) va_n = v_operand(0);
-
-      // ---- running max of tile t; a rescale it calls for applies to l now and
-      // to O at the start of the next stage, after PV(t-1).
+    };
+    // Running max of tile t; a rescale it calls for applies to l now and to O
+    // at the start of the next stage, after PV(t-1).  Returns the reference
+    // the weights of tile t are taken against.
+    auto softmax_ref = [&](f32x16_t (&sc)[2], int t) {
       if (t >= n_clean || t < n_lo) mask(sc, t);
       float mx = sc[0][0];
 #pragma unroll
@@ -445,7 +432,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         l1 *= pend_alpha;
         m = mn;
       }
-      const float mu = (m == -INFINITY) ? 0.f : m;
+      return (m == -INFINITY) ? 0.f : m;
+    };
+    auto stage_end = [&]() {
+      wait_all_vmem();  // this wave's direct loads have landed
+      __syncthreads();  // ... and every other wave's
+    };
+
+    auto stage = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t,
+                     bool with_pv) {
+      const int kb_next = (t + 1) & 1;  // K(t+1)
+      stage_start(t);
+
+      // Operands of group j of the interleave below (QK^T k-step j % KS of
+      // key block j / KS, and PV MFMA j), read from LDS one group ahead of
+      // their MFMAs so that no MFMA waits for an LDS read it just issued.
+      auto k_operand = [&](int j) {
+        return *reinterpret_cast<const bf16x8_t*>(&sm.k[kb_next][k_off(j / KS, j % KS)]);
+      };
+      auto v_operand = [&](int j) {
+        const int kk = j / DB, db = j % DB;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 0, db)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm.v[(t - 1) & 1] + v_off(kk, 1, db)));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8_t ka_n = k_operand(0), va_n{};
+      if (with_pv) va_n = v_operand(0);
+
+      const float mu = softmax_ref(sc, t);
 
       // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t),
       // packed to bf16 pairs as they are made.  PV(t-1) has 4 * DB = 2 * KS
@@ -487,8 +501,53 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       }
       pin(l0);
       pin(l1);
-      wait_all_vmem();  // this wave's direct loads have landed
-      __syncthreads();  // ... and every other wave's
+      stage_end();
+    };
+
+    // The last stages of a wave near the causal diagonal.  Wave w's rows see
+    // no key of tiles te_w and later (their weights would be exact zeros):
+    // once S(te_w) would be next, the wave drops the products that only such
+    // tiles feed and keeps copying its share of the tiles and meeting the
+    // barriers.  SOFTMAX: the weights of tile t (sc -> pc); PV: O += V(t-1)
+    // P(t-1) (pp), each V^T operand read one MFMA ahead.
+    auto stage_part = [&](f32x16_t (&sc)[2], const bf16x8_t (&pp)[4], bf16x8_t (&pc)[4], int t, auto softmax,
+                          auto with_pv) {
+      stage_start(t);
+      if constexpr (decltype(softmax)::value) {
+        const float mu = softmax_ref(sc, t);
+        u32x4_t w[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(sc[kb][r], c, -mu));
+            const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c, -mu));
+            l0 += p0;
+            l1 += p1;
+            w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pc[i] = __builtin_bit_cast(bf16x8_t, w[i]);
+      }
+      if constexpr (decltype(with_pv)::value) {
+        const uint16_t* vt = sm.v[(t - 1) & 1];
+        auto v_op = [&](int j) {
+          const int kk = j / DB, db = j % DB;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_off(kk, 0, db)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_off(kk, 1, db)));
+          return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8_t va_n = v_op(0);
+#pragma unroll
+        for (int j = 0; j < 4 * DB; ++j) {
+          const bf16x8_t va = va_n;
+          if (j + 1 < 4 * DB) va_n = v_op(j + 1);
+          oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[j / DB], oacc[j % DB], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+      stage_end();
     };
 
     f32x16_t s_a[2], s_b[2];
@@ -514,22 +573,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     __syncthreads();  // K buffer of tile tb is refilled by the first stage
 
     if (te > tb) {
+      using yes = std::true_type;
+      using no = std::false_type;
       stage(s_a, s_b, p_b, p_a, tb, false);
       int t = tb + 1;
-      for (; t + 1 < te; t += 2) {
+      // full stages while S(t+1) still has a key this wave sees
+      const int t_full = min(te, te_w);
+      for (; t + 1 < t_full; t += 2) {
         stage(s_b, s_a, p_a, p_b, t, true);
         stage(s_a, s_b, p_b, p_a, t + 1, true);
       }
-      if (t < te) stage(s_b, s_a, p_a, p_b, t, true);
-      // drain: a due rescale, then PV of the last tile
+      const int t_loop = t;  // stages from here on alternate buffers as stage t of the loop would
+      if (t < te && t == te_w - 1) {  // weights of this wave's last tile and PV(t-1), then PV(t)
+        stage_part(s_b, p_a, p_b, t, yes{}, yes{});
+        if (++t < te) stage_part(s_a, p_b, p_a, t++, no{}, yes{});
+      } else if (t < te && t == te_w) {  // PV of this wave's last tile
+        stage_part(s_b, p_a, p_b, t++, no{}, yes{});
+      }
+      for (; t < te; ++t) stage_part(s_b, p_a, p_b, t, no{}, no{});  // copies and barriers only
+      // drain: a due rescale, then PV of the last tile when this wave sees it
       if (pending) {
 #pragma unroll
         for (int i = 0; i < DB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[i][r] *= pend_alpha;
       }
-      if (t < te) pv(p_b, t & 1);
-      else pv(p_a, (t - 1) & 1);
+      if (te_w >= te) {
+        if (t_loop < te) pv(p_b, (te - 1) & 1);
+        else pv(p_a, (te - 1) & 1);
+      }
     }
 
     // ---- epilogue: one division, bf16 output, natural-log LSE.  O leaves
