@@ -47,7 +47,12 @@
 //     counts add up to the same total for every pair, so all workgroups of a
 //     launch carry equal work; workgroups that share a KV head are placed on
 //     the same XCD (dispatch is round-robin over the 8 XCDs) so that head's
-//     K/V stays in that XCD's L2.
+//     K/V stays in that XCD's L2.  On the diagonal, a wave stops its
+//     products at the first key tile that all of its 32 rows mask (their
+//     weights would be exact zeros) and from there on only copies its share
+//     of the tiles and meets the barriers.
+//   * the output tile leaves through LDS (the K/V tiles are free by then), so
+//     that each global store writes 1 KiB of consecutive rows.
 //   * the row sum is accumulated in fp32 from the unrounded weights (a sum of
 //     the bf16-rounded weights would move the log-sum-exp by ~1e-3 on short
 //     rows).
