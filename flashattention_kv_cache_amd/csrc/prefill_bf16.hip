@@ -271,6 +271,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     const int n_lo = W > 0 ? (max(0, last_row + off - W + 1) + kBN - 1) / kBN : 0;
     // causal: tiles [tb, te_w) hold a key that some row of this wave sees
     const int te_w = a.causal ? min(te, max(tb, (min(q0 + wave * 32 + 31, a.Nq - 1) + off) / kBN + 1)) : te;
+    // window: this wave's rows see no key before tile tl_w; when tl > tb the
+    // wave skips the products of tiles tb .. tl - 1 (exact zeros) and starts
+    // its pipeline at tl
+    const int tl_w = W > 0 ? max(0, q0 + wave * 32 + off - W + 1) / kBN : tb;
+    const int tl = (tl_w > tb && tl_w < te_w) ? tl_w : tb;
 
     // ---- Q^T operand fragments, kept in registers
     const int qrow = q0 + wave * 32 + col;
@@ -574,14 +579,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     }
     wait_all_vmem();
     __syncthreads();
-    if (te > tb) qk(s_a, tb & 1);
+    if (te > tb && tl == tb) qk(s_a, tb & 1);
     __syncthreads();  // K buffer of tile tb is refilled by the first stage
 
     if (te > tb) {
       using yes = std::true_type;
       using no = std::false_type;
-      stage(s_a, s_b, p_b, p_a, tb, false);
-      int t = tb + 1;
+      // a late window start: copies and barriers only, then S(tl) alone; the
+      // register buffers then alternate from tl as they would from tb
+      for (int u = tb; u < tl - 1; ++u) stage_part(s_b, p_a, p_b, u, no{}, no{});
+      if (tl > tb) {
+        stage_start(tl - 1);
+        qk(s_a, tl & 1);
+        stage_end();
+      }
+      stage(s_a, s_b, p_b, p_a, tl, false);
+      int t = tl + 1;
       // full stages while S(t+1) still has a key this wave sees
       const int t_full = min(te, te_w);
       for (; t + 1 < t_full; t += 2) {
