@@ -442,7 +442,7 @@ def main():
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "N": wp.Nq, "d": wp.d, "causal": True,
                         "seed": wp.seed, "flops": flops},
             "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "block_size": wd.block_size,
-                       "len_range": [wd.len_lo, wd.len_hi], "seed": wd.seed, "tokens": kv_bytes // 4096,
+                       "len_range": [wd.len_lo, wd.len_hi], "seed": wd.seed, "tokens": kv_bytes // wd.kv_bytes_per_token(),
                        "split_tokens": split, "bytes": dec_bytes},
         },
         "prefill": {"value": round(tflops, 3), "unit": "TFLOP/s", "kernel_ms": round(pre_avg, 5),

@@ -85,6 +85,37 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out_tensor(out: Optional[torch.Tensor], shape, dtype, device, name: str) -> torch.Tensor:
+    """A caller-supplied output must be exactly what the kernel writes: the
+    library receives only its address, so a smaller or differently typed
+    buffer would be written past its end."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(out, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {out.dtype} {tuple(out.shape)}")
+    if out.device != device:
+        raise ValueError(f"{name} must be on {device}, got {out.device}")
+    if not out.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return out
+
+
+def _lse_tensor(lse: Optional[torch.Tensor], want: bool, shape, device) -> Optional[torch.Tensor]:
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=device) if want else None
+    return _out_tensor(lse, shape, torch.float32, device, "lse")
+
+
+def _workspace_bytes(ws: Optional[torch.Tensor], device) -> int:
+    if ws is None:
+        return 0
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return ws.numel() * ws.element_size()
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -110,10 +141,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
         raise ValueError("q, k, v disagree in batch, head dim or dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
+    lse = _lse_tensor(lse, want_lse, (B, Hq, Nq), q.device)
     _check(lib().fa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                             B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window), float(scale),
                             _dtype_code(q), _stream(stream)))
@@ -180,13 +209,11 @@ def decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, se
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, Hq, c.Hkv, d, max_seq_len, split_tokens, window)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    if need and _workspace_bytes(workspace, q.device) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
+    lse = _lse_tensor(lse, want_lse, (B, Hq), q.device)
+    ws_bytes = _workspace_bytes(workspace, q.device)
     _check(lib().fa_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
                                c.block_size, c.max_blocks, c.capacity, int(max_seq_len), int(window),
                                _ptr(out), _ptr(lse), B, Hq, c.Hkv, d, float(scale), float(k_scale),
@@ -249,10 +276,8 @@ def chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         max_seq_len = c.bound
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
+    lse = _lse_tensor(lse, want_lse, (B, Hq, Nq), q.device)
     _check(lib().fa_chunked_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
                                     c.block_size, c.max_blocks, c.capacity, int(max_seq_len),
                                     _ptr(out), _ptr(lse), B, Hq, c.Hkv, Nq, d, int(bool(causal)), int(window),
@@ -289,13 +314,11 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, split_tokens, window)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    if need and _workspace_bytes(workspace, q.device) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
+    lse = _lse_tensor(lse, want_lse, (B, Hq), q.device)
+    ws_bytes = _workspace_bytes(workspace, q.device)
     _check(lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
                            block_size if paged else 0, max_blocks, capacity, int(max_seq_len), int(window),
                            _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
@@ -346,13 +369,11 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, seq_lens: torch.Tensor, 
     if max_seq_len is None:
         max_seq_len = bound
     need = mla_decode_workspace_bytes(B, Hq, max_seq_len, split_tokens)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    if need and _workspace_bytes(workspace, q.device) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, Hq, MLA_DC), dtype=torch.bfloat16, device=q.device)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    out = _out_tensor(out, (B, Hq, MLA_DC), torch.bfloat16, q.device, "out")
+    lse = _lse_tensor(lse, want_lse, (B, Hq), q.device)
+    ws_bytes = _workspace_bytes(workspace, q.device)
     _check(lib().fa_mla_decode(_ptr(q), _ptr(kv_cache), _ptr(seq_lens), _ptr(block_table), bs, max_blocks, capacity,
                                int(max_seq_len), _ptr(out), _ptr(lse), B, Hq, MLA_DC, MLA_DR, float(scale),
                                int(split_tokens), _ptr(workspace) if need else None, ws_bytes, _stream(stream)))

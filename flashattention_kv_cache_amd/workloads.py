@@ -134,6 +134,11 @@ class DecodeWorkload:
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
+    def kv_bytes_per_token(self) -> int:
+        """Cache bytes one cached token occupies in one layer (its key and value
+        for every KV head): the bytes a decode step reads per cached token."""
+        return 2 * self.Hkv * self.d * (1 if self.dtype == "fp8" else _DTYPES[self.dtype].itemsize)
+
 
 def prefill_inputs(w: PrefillWorkload):
     """(q, k, v) on the CPU for a prefill workload."""

@@ -18,7 +18,10 @@
  *   - The library is stateless apart from a thread-local error message and is
  *     safe to call from several host threads.
  *   - Outputs are deterministic: the same inputs and launch configuration give
- *     the same bits (no atomics).
+ *     the same bits.  No kernel accumulates a result with atomics; the only
+ *     atomics are the LDS counters with which fa_mla_decode's planning step
+ *     orders its work list, and they decide only which workgroup runs which
+ *     split, never a value that is written.
  */
 #ifndef FA_H
 #define FA_H

@@ -235,6 +235,50 @@ def test_p6_kv_bytes_table():
         assert got == e["value"] * unit[e["unit"]], e["what"]
 
 
+def _pin_bytes_per_token(fn):
+    """Per-token figures the pages print: per token per layer (layers = 1),
+    per head (kv_heads = 1) and per token over all layers."""
+    for e in golden("kv_cache_sizes.json")["exact_bytes"]:
+        if e["tokens"] == 1 and e["batch"] == 1:
+            assert fn(e["layers"], e["kv_heads"], e["head_dim"], e["bytes_per_elem"]) == e["bytes"], e["what"]
+    unit = {"KiB": 2 ** 10, "MiB": 2 ** 20, "GiB": 2 ** 30}
+    for e in golden("kv_cache_sizes.json")["binary_units"]:
+        if e["tokens"] == 1 and e["batch"] == 1:
+            assert fn(e["layers"], e["kv_heads"], e["head_dim"], 2) == e["value"] * unit[e["unit"]], e["what"]
+    # Llama 3 70B ("KV Cache, Flash Attention and Inference Optimization", KV
+    # cache sizing): 4,096 B per token per layer in fp16, so 80 layers x 32,000
+    # tokens is the printed ~10.4 GB (10.49e9 B)
+    assert fn(1, 8, 128, 2) == 4096
+    assert abs(fn(80, 8, 128, 2) * 32000 / 1e9 - 10.4) < 0.1
+    # "Генерация и KV-кэш", "Сколько весит KV-кэш": 2 bytes per number in
+    # BF16, 1 in FP8, so an FP8 cache is half the size
+    assert fn(1, 8, 128, 1) * 2 == fn(1, 8, 128, 2)
+
+
+def test_p6_kv_bytes_per_token():
+    _pin_bytes_per_token(oracle.kv_bytes_per_token)
+
+
+@pytest.mark.parametrize("kind", ["no_kv_factor", "ignores_dtype", "query_heads"])
+def test_p6_planted_per_token_mistakes_are_caught(kind):
+    def mutant(layers, kv_heads, head_dim, bytes_per_elem=2):
+        if kind == "no_kv_factor":
+            return layers * kv_heads * head_dim * bytes_per_elem
+        if kind == "ignores_dtype":
+            return 2 * layers * kv_heads * head_dim * 2
+        return 2 * layers * (4 * kv_heads) * head_dim * bytes_per_elem  # counts query heads (n_rep = 4)
+    with pytest.raises(AssertionError):
+        _pin_bytes_per_token(mutant)
+
+
+def test_p6_decode_workload_bytes_per_token():
+    """The benchmark's byte count of a cached token equals the formula."""
+    from flashattention_kv_cache_amd import workloads as W
+    for w in (W.C3, W.C5, W.WINDOW_DECODE):
+        assert w.kv_bytes_per_token() == oracle.kv_bytes_per_token(1, w.Hkv, w.d, 2) == 4096
+    assert W.FP8_DECODE.kv_bytes_per_token() == oracle.kv_bytes_per_token(1, 8, 128, 1) == 2048
+
+
 def test_p6_decode_workload_kv_bytes_match_formula():
     di = make_decode_inputs(5, 8, 2, 64, "bf16", 9, len_range=(3, 40))
     total = int(di.seq_lens.sum())
