@@ -154,17 +154,13 @@ def prefill_rows(q, k, v, scale: float, causal: bool, rows, window: int = 0):
 
 def paged_gather(pool, table_row, L: int, g: int, block_size: int):
     """Rows 0..L-1 of KV head g of one sequence, read through its block table:
-    token t comes from pool[table_row[t // block_size], t % block_size, g]."""
-    table_row = _i64(table_row)
-    nblk = (L + block_size - 1) // block_size
-    out = []
-    for j in range(nblk):
-        blk = int(table_row[j])
-        n = min(block_size, L - j * block_size)
-        out.append(_f64(pool[blk, :n, g]))
-    if not out:
+    token t comes from pool[table_row[t // block_size], t % block_size, g]
+    (one indexed read of all L tokens, written as that formula)."""
+    if L == 0:
         return np.zeros((0, pool.shape[-1]))
-    return np.concatenate(out, axis=0)
+    t = np.arange(L)
+    blk = _i64(table_row)[t // block_size]
+    return _f64(pool[blk, t % block_size, g])
 
 
 def decode_contiguous(q, k_cache, v_cache, seq_lens, scale: float, heads=None, window: int = 0):

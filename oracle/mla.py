@@ -74,13 +74,15 @@ def mla_decode_latent(q, kv, seq_lens, scale: float, d_c: int, block_table=None,
     O = np.full((B, H, d_c), np.nan)
     lse = np.full((B, H), np.nan)
     todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    rows = {}
+    # every head of a sequence attends the same cache rows: one score matrix
+    # per sequence, one row per requested head
+    by_seq = {}
     for b, h in todo:
-        if b not in rows:
-            rows[b] = _rows(kv, b, int(lens[b]), block_table, block_size)
-        K = rows[b]
-        o, l = attention_rows(_f64(q[b, h:h + 1]), K, K[:, :d_c], scale)
-        O[b, h], lse[b, h] = o[0], l[0]
+        by_seq.setdefault(b, []).append(h)
+    for b, hs in by_seq.items():
+        K = _rows(kv, b, int(lens[b]), block_table, block_size)
+        o, l = attention_rows(_f64(q[b, hs]), K, K[:, :d_c], scale)
+        O[b, hs], lse[b, hs] = o, l
     return O, lse
 
 

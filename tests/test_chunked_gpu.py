@@ -229,18 +229,7 @@ def test_chunked_workload_full_size(fa):
     # the append: the whole pool, bit for bit
     kr, vr = oracle_append(ci)
     assert torch.equal(bits(kc), bits(kr)) and torch.equal(bits(vc), bits(vr))
-    # sampled rows: first and last query of every sequence, the 64/128-row tile
-    # edges, and random ones
-    rng = np.random.default_rng(7)
-    rows = []
-    for b in range(w.B):
-        for i in (0, 63, 64, 127, 128, w.chunk - 1):
-            rows.append((b, int(rng.integers(w.Hq)), i))
-    rows += [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.chunk))) for _ in range(24)]
-    O_ref, lse_ref = oracle.chunked_prefill(ci.q, kr, vr, ci.seq_lens, w.scale, True, ci.block_table,
-                                            w.block_size, rows=rows)
-    idx = tuple(torch.tensor(c) for c in zip(*rows))
-    check(o.cpu()[idx], lse.cpu()[idx], O_ref, lse_ref, "bf16", "chunked workload rows")
-    # properties that hold everywhere: finite, LSE no smaller than the
-    # largest visible score would allow for one key (checked as finite here)
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # every output row and LSE against the oracle
+    note("chunked workload: oracle over every row")
+    O_ref, lse_ref = oracle.chunked_prefill(ci.q, kr, vr, ci.seq_lens, w.scale, True, ci.block_table, w.block_size)
+    check(o.cpu(), lse.cpu(), O_ref, lse_ref, "bf16", "chunked workload, every output")

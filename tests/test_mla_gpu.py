@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import full_size as FS
 import oracle
 from oracle import mla as M
 from flashattention_kv_cache_amd import workloads as W
@@ -109,21 +110,19 @@ def test_mla_kernel_implements_the_absorbed_model(fa):
 
 
 def test_mla_decode_full_size(fa):
+    """The DeepSeek-V3-shaped MLA batch in the benchmark's launch
+    configuration: every (sequence, head) output and LSE against the oracle."""
     w = W.MLA_DECODE
     note(f"mla decode {w.name}")
     mi = W.mla_inputs(w)
     o, lse = fa.mla_decode(mi.q.to(DEV), mi.kv.to(DEV), mi.seq_lens.to(DEV), w.scale,
                            block_table=mi.block_table.to(DEV), max_seq_len=mi.max_seq_len)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(14)
-    order = np.argsort(mi.seq_lens.numpy())
-    bsel = sorted({int(order[0]), int(order[-1])} | {int(x) for x in rng.integers(0, w.B, 4)})
-    heads = [(b, h) for b in bsel for h in rng.choice(w.Hq, 4, replace=False).tolist()]
-    O_ref, lse_ref = M.mla_decode_latent(mi.q, mi.kv, mi.seq_lens, w.scale, 512, mi.block_table, w.block_size,
-                                         heads=heads)
-    idx = tuple(torch.tensor(c) for c in zip(*heads))
-    check(o.cpu()[idx], lse.cpu()[idx], O_ref[idx], lse_ref[idx], "mla full size")
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    note("mla decode: oracle over the whole batch")
+    O_ref, lse_ref = FS.decode_batches(
+        lambda heads: M.mla_decode_latent(mi.q, mi.kv, mi.seq_lens, w.scale, 512, mi.block_table, w.block_size,
+                                          heads=heads), w.B, w.Hq)
+    check(o.cpu(), lse.cpu(), O_ref, lse_ref, "mla full size, every output")
 
 
 def _expected_items(lens, max_seq_len, st):

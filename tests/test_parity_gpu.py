@@ -4,9 +4,11 @@ Tolerances: fp32 inputs, max-abs 1e-5 on O; bf16 inputs with fp32 accumulation,
 max-abs 2e-2 and mean-abs 2e-3 on O; LSE within 1e-4 (rows with no visible key
 must give exactly O = 0 and LSE = -inf on both sides).
 
-Small shapes compare every output element; the five full-size workloads run in
-the launch configuration the benchmark times and compare sampled rows, which
-the oracle computes one by one, plus properties that hold at any size.
+Small shapes compare every output element.  The full-size workloads run in
+the launch configuration the benchmark times: the N = 4096 prefill and both
+decode batches compare every output element and LSE; the N = 32768 prefill
+compares every row of one query head per KV head (all query-tile pairs, every
+KV head) plus rows sampled over all heads.
 """
 import math
 import sys
@@ -15,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import full_size as FS
 import oracle
 from flashattention_kv_cache_amd import workloads as W
 
@@ -244,8 +247,35 @@ def _sample_rows(w, rng, n_random):
     return rows
 
 
-@pytest.mark.parametrize("w", [W.C2, W.C4], ids=["C2_N4096", "C4_N32768"])
-def test_workload_prefill_full_size(fa, w):
+def one_head_per_kv_head(w):
+    """A query head of every KV head, each at a different position within its
+    group: every KV head (and with it every XCD slot of the launch's
+    KV-head-major mapping) and every query-tile pair is covered."""
+    n_rep = w.Hq // w.Hkv
+    return [(b, g * n_rep + (g + b) % n_rep) for b in range(w.B) for g in range(w.Hkv)]
+
+
+def test_workload_prefill_full_size_C2_every_output(fa):
+    """The N = 4096 workload in the benchmark's launch configuration, every
+    output element and every LSE against the oracle."""
+    w = W.C2
+    note(f"{w.name}: generating inputs")
+    q, k, v = W.prefill_inputs(w)
+    note(f"{w.name}: launching")
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    note(f"{w.name}: oracle over all {w.B * w.Hq} heads")
+    ref = FS.prefill_heads(q, k, v, w.scale, w.causal, [(b, h) for b in range(w.B) for h in range(w.Hq)])
+    O_ref = np.stack([np.stack([ref[(b, h)][0] for h in range(w.Hq)]) for b in range(w.B)])
+    L_ref = np.stack([np.stack([ref[(b, h)][1] for h in range(w.Hq)]) for b in range(w.B)])
+    err = check(o_c, lse_c, O_ref, L_ref, "bf16", w.name)
+    note(f"{w.name}: all {o_c.numel()} outputs, max abs err {err:.2e}")
+
+
+@pytest.fixture(scope="module")
+def c4_run(fa):
+    w = W.C4
     note(f"{w.name}: generating inputs")
     q, k, v = W.prefill_inputs(w)
     note(f"{w.name}: launching")
@@ -253,7 +283,26 @@ def test_workload_prefill_full_size(fa, w):
     torch.cuda.synchronize()
     o_c, lse_c = o.cpu(), lse.cpu()
     del o, lse
+    torch.cuda.empty_cache()
+    return w, q, k, v, o_c, lse_c
+
+
+def test_workload_prefill_full_size_C4_whole_heads(c4_run):
+    """N = 32768: every row of one query head per KV head (all 64 query-tile
+    pairs of the launch, every KV head) against the oracle."""
+    w, q, k, v, o_c, lse_c = c4_run
     assert torch.isfinite(o_c.float()).all() and torch.isfinite(lse_c).all()
+    heads = one_head_per_kv_head(w)
+    note(f"{w.name}: oracle over heads {heads}")
+    ref = FS.prefill_heads(q, k, v, w.scale, w.causal, heads)
+    for b, h in heads:
+        err = check(o_c[b, h], lse_c[b, h], ref[(b, h)][0], ref[(b, h)][1], "bf16", f"{w.name} head {h}")
+        note(f"{w.name}: head {h}, all {w.Nq} rows, max abs err {err:.2e}")
+
+
+def test_workload_prefill_full_size_C4_sampled_rows(c4_run):
+    """N = 32768: rows sampled over all heads (tile edges and random)."""
+    w, q, k, v, o_c, lse_c = c4_run
     rows = _sample_rows(w, np.random.default_rng(w.seed), 48)
     O_ref, lse_ref = oracle.prefill_rows(q, k, v, w.scale, w.causal, rows)
     got = torch.stack([o_c[b, h, i] for b, h, i in rows])
@@ -263,7 +312,9 @@ def test_workload_prefill_full_size(fa, w):
 
 
 @pytest.mark.parametrize("w", [W.C3, W.C5], ids=["C3_contiguous", "C5_paged"])
-def test_workload_decode_full_size(fa, w):
+def test_workload_decode_full_size_every_output(fa, w):
+    """The decode workloads in the benchmark's launch configuration (library
+    split choice), every (sequence, head) output and LSE against the oracle."""
     note(f"{w.name}: generating inputs")
     di = W.decode_inputs(w)
     note(f"{w.name}: launching")
@@ -273,19 +324,13 @@ def test_workload_decode_full_size(fa, w):
     o, lse = fa.decode(di.q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.seq_lens.to(DEV), **kwargs)
     torch.cuda.synchronize()
     o_c, lse_c = o.cpu(), lse.cpu()
-    assert torch.isfinite(o_c.float()).all() and torch.isfinite(lse_c).all()
-    rng = np.random.default_rng(w.seed)
-    lens = di.seq_lens.numpy()
-    pick_b = sorted({int(lens.argmax()), int(lens.argmin()), 0, w.B - 1} | {int(x) for x in rng.integers(w.B, size=12)})
-    heads = [(b, h) for b in pick_b for h in range(w.Hq)]
+    note(f"{w.name}: oracle over all {w.B} sequences")
     if di.paged:
-        O_ref, lse_ref = oracle.decode_paged(di.q, di.k_cache, di.v_cache, di.block_table, di.seq_lens,
-                                             di.block_size, w.scale, heads=heads)
+        fn = lambda heads: oracle.decode_paged(di.q, di.k_cache, di.v_cache, di.block_table, di.seq_lens,  # noqa: E731
+                                               di.block_size, w.scale, heads=heads)
     else:
-        O_ref, lse_ref = oracle.decode_contiguous(di.q, di.k_cache, di.v_cache, di.seq_lens, w.scale, heads=heads)
-    got = torch.stack([o_c[b, h] for b, h in heads])
-    got_lse = torch.stack([lse_c[b, h] for b, h in heads])
-    ref = np.stack([O_ref[b, h] for b, h in heads])
-    ref_lse = np.array([lse_ref[b, h] for b, h in heads])
-    err = check(got, got_lse, ref, ref_lse, "bf16", w.name)
-    note(f"{w.name}: {len(heads)} sampled (sequence, head) rows, max abs err {err:.2e}")
+        fn = lambda heads: oracle.decode_contiguous(di.q, di.k_cache, di.v_cache, di.seq_lens, w.scale,  # noqa: E731
+                                                    heads=heads)
+    O_ref, L_ref = FS.decode_batches(fn, w.B, w.Hq)
+    err = check(o_c, lse_c, O_ref, L_ref, "bf16", w.name)
+    note(f"{w.name}: all {w.B * w.Hq} (sequence, head) rows, max abs err {err:.2e}")
