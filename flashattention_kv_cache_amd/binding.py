@@ -30,6 +30,7 @@ SIGNATURES = {
     "fa_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P], _I),
     "fa_kv_append": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P], _I),
     "fa_chunked_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
+    "fa_decode_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P], _I),
     "fa_decode_fp8": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _F, _F, _I, _P, _S, _P], _I),
     "fa_kv_append_fp8": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P], _I),
     "fa_mla_decode": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P], _I),
@@ -324,6 +325,30 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
                            _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
                            int(split_tokens), _ptr(workspace) if need else None, ws_bytes,
                            _stream(stream)))
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                   block_table: Optional[torch.Tensor] = None, block_size: int = 0,
+                   max_seq_len: Optional[int] = None, scale: Optional[float] = None, split_tokens: int = 0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   want_lse: bool = True, window: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fa_decode_noalloc: ``decode`` without a workspace; the library keeps
+    the split partials in a fixed scratch array on each GPU (no device
+    allocation by the library).  Pass ``out`` (and ``lse``) to allocate nothing
+    here either."""
+    B, Hq, d = q.shape
+    c = _cache_layout(q, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
+    if max_seq_len is None:
+        max_seq_len = c.bound
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
+    lse = _lse_tensor(lse, want_lse, (B, Hq), q.device)
+    _check(lib().fa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+                                   c.block_size if c.paged else 0, c.max_blocks, c.capacity, int(max_seq_len),
+                                   int(window), _ptr(out), _ptr(lse), B, Hq, c.Hkv, d, float(scale), _dtype_code(q),
+                                   int(split_tokens), _stream(stream)))
     return out, lse
 
 

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa_internal.h"
 
 namespace {
@@ -142,7 +144,7 @@ int max_splits_for(int max_seq_len, int split_tokens) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 5; }
+int fa_abi_version(void) { return 6; }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
@@ -283,13 +285,45 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len,
 
 namespace {
 
+// Split partials of fa_decode_noalloc: one array per GPU, in the code object's
+// device memory, so that call allocates nothing.  In host code `scratch` names
+// a host-side stand-in; its device address comes from hipGetSymbolAddress,
+// looked up once per device (with that device current) and kept here.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FA_ERR_HIP, "scratch address lookup on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 // fa_decode and fa_decode_fp8 share everything but the cache element type.
+// static_scratch: the split partials go to this device's scratch array
+// (workspace and workspace_bytes are ignored).
 int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seq_lens, const int32_t* block_table,
                 int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
                 void* o, float* lse,
                 int B, int Hq, int Hkv, int d, float scale, fa::KvType kv, float k_scale, float v_scale,
-                int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                bool static_scratch = false) {
   int st0 = check_decode_sizes(B, Hq, Hkv, d, max_seq_len, split_tokens);
   if (st0 != FA_OK) return st0;
   if (check_window(window, 1) != FA_OK) return FA_ERR_INVALID;
@@ -320,7 +354,13 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   const int stoks = split_tokens ? split_tokens : choose_split_tokens(B, Hq, Hkv, span);
   const int ns = max_splits_for(span, stoks);
   const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, window, split_tokens);
-  if (need > 0) {
+  if (static_scratch) {
+    if (need > (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES)
+      return fail(FA_ERR_UNSUPPORTED, "split partials need %zu bytes, more than the %zu-byte scratch array",
+                  need, (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES);
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else if (need > 0) {
     if (!workspace) return fail(FA_ERR_INVALID, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
       return fail(FA_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
@@ -328,6 +368,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   }
   if (B > 65535 || Hq > 65535 || ns > 65535)
     return fail(FA_ERR_UNSUPPORTED, "grid too large (B, Hq and the number of splits must be <= 65535)");
+  if (static_scratch && need > 0) {  // every argument checked: now the (first-call) address lookup
+    const int sc = current_scratch(&workspace);
+    if (sc != FA_OK) return sc;
+  }
 
   fa::DecodeArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.block_table = block_table;
@@ -365,6 +409,18 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
                      max_seq_len, window, o, lse, B, Hq, Hkv, d, scale,
                      dtype == FA_BF16 ? fa::KvType::BF16 : fa::KvType::F32, 1.f, 1.f,
                      split_tokens, workspace, workspace_bytes, stream);
+}
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, const int32_t* block_table,
+                      int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
+                      void* o, float* lse,
+                      int B, int Hq, int Hkv, int d, float scale, int dtype, int split_tokens, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  return decode_impl(q, k_cache, v_cache, seq_lens, block_table, block_size, max_blocks_per_seq, kv_capacity,
+                     max_seq_len, window, o, lse, B, Hq, Hkv, d, scale,
+                     dtype == FA_BF16 ? fa::KvType::BF16 : fa::KvType::F32, 1.f, 1.f,
+                     split_tokens, nullptr, 0, stream, /*static_scratch=*/true);
 }
 
 int fa_decode_fp8(const void* q, const void* k_cache, const void* v_cache,

@@ -170,6 +170,33 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache,
               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_noalloc — fa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, same kernels and the same results bit for
+ * bit as fa_decode with the same split_tokens, but without the workspace: the
+ * split partials go to a scratch array that the library holds in each GPU's
+ * memory (FA_DECODE_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends; its address is looked up on the first call on each device).  Nothing
+ * is allocated or freed by this call, on the host or the device.
+ *
+ * Sizes whose partials exceed the array (fa_decode_workspace_bytes(...) >
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_UNSUPPORTED and enqueue
+ * nothing.  The array's contents on entry are ignored (every partial that is
+ * read was written by the same call) and it keeps the last call's partials.
+ * All calls on one GPU share the array: calls that may overlap on one GPU
+ * (different streams without ordering between them) race and give undefined
+ * results; calls on one stream are ordered and safe.  The stream must belong
+ * to the current device.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, const int32_t* block_table,
+                      int block_size, int max_blocks_per_seq, int kv_capacity, int max_seq_len, int window,
+                      void* o, float* lse,
+                      int B, int Hq, int Hkv, int d, float scale, int dtype, int split_tokens, void* stream);
+
+/*
  * fa_decode_fp8 — fa_decode against a cache of FP8 codes: one byte per cached
  * number instead of two, so a decode step reads half the bytes.
  *

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(fa):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(fa.SIGNATURES) == set(declared_functions())
-    assert L.fa_abi_version() == 5
+    assert L.fa_abi_version() == 6
 
 
 def test_status_strings(fa):
@@ -145,6 +145,42 @@ def test_decode_split_choice(fa):
     assert L.fa_decode_split_tokens(2, 8, 3, 128, 100, 0) == 0
     # a window shorter than the longest sequence sizes the splits by the window
     assert L.fa_decode_split_tokens(128, 32, 8, 128, 32768, 1024) == L.fa_decode_split_tokens(128, 32, 8, 128, 1024, 0)
+
+
+def decode_noalloc(fa, q=A, k=A, v=A, lens=A, table=None, bs=16, mbps=4, cap=64, maxlen=64, window=0, o=A, lse=A,
+                   B=2, Hq=8, Hkv=2, d=128, scale=0.1, dtype=BF16, split=0):
+    P = ctypes.c_void_p
+    return fa.lib().fa_decode_noalloc(P(q), P(k), P(v), P(lens), P(table), bs, mbps, cap, maxlen, window, P(o),
+                                      P(lse), B, Hq, Hkv, d, scale, dtype, split, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), FA_ERR_INVALID, "divide"),
+    (dict(d=80), FA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=5), FA_ERR_INVALID, "dtype"),
+    (dict(split=100), FA_ERR_INVALID, "multiple of 256"),
+    (dict(table=A, bs=12), FA_ERR_INVALID, "power of two"),
+    (dict(q=0), FA_ERR_INVALID, "null"),
+    (dict(k=MIS), FA_ERR_INVALID, "aligned"),
+    # split partials larger than the scratch array: 128 x 32 heads x 128 splits x 129 floats
+    (dict(B=128, Hq=32, Hkv=8, maxlen=32768, cap=32768, split=256), FA_ERR_UNSUPPORTED, "scratch"),
+])
+def test_decode_noalloc_rejects(fa, kw, status, msg):
+    """The no-allocation decode checks its arguments like fa_decode (before
+    any HIP call), and refuses sizes whose partials exceed its scratch array."""
+    assert decode_noalloc(fa, **kw) == status
+    assert msg in fa.lib().fa_last_error().decode()
+
+
+def test_decode_noalloc_scratch_limit_matches_header(fa):
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    limit = int(m.group(1)) << int(m.group(2))
+    L = fa.lib()
+    # the benchmark's paged decode batch fits (128 x 32 heads, up to 32768 tokens, library split)
+    st = L.fa_decode_split_tokens(128, 32, 8, 128, 32768, 0)
+    assert 0 < L.fa_decode_workspace_bytes(128, 32, 8, 128, 32768, 0, st) <= limit
+    assert L.fa_decode_workspace_bytes(128, 32, 8, 128, 32768, 0, 256) > limit
 
 
 def test_decode_empty_batch_is_a_noop(fa):
