@@ -15,7 +15,8 @@ Printed: one JSON line.  ``value`` is prefill TFLOP/s (algorithmic flops:
 object holds the decode KV GB/s (algorithmic bytes: every cached K/V byte once,
 plus q, o, lse and the block-table entries read).  Kernel durations come from
 HIP events recorded around each launch on the stream the kernels run on.
-``extras`` (outside the step, skipped with --no-extras) times the KV append,
+``extras`` (outside the step, skipped with --no-extras; run before the
+warm-up, see ``preconditioning``) times the KV append,
 the chunked prefill against a paged cache, sliding-window prefill and decode,
 decode against an FP8 cache, the long-context prefill (N = 32768) and decode
 against a contiguous cache, and MLA decode, each on its own.
@@ -386,6 +387,19 @@ def main():
         binding.decode(dq, dk, dv, dl, block_table=dt_, max_seq_len=wd.len_hi, scale=wd.scale,
                        split_tokens=split, workspace=ws, out=do, lse=dlse)
 
+    # The measurements outside the step run first: they keep the GPU busy for
+    # a second or more, so the timed steps see the clocks a GPU under
+    # continuous load holds (after a few milliseconds of idle-to-busy, prefill
+    # launches run up to 30% slower for the first ~20 steps while the clocks
+    # settle).  With --no-extras, the W warm-up steps are all the warm-up.
+    extra = None
+    busy_s = 0.0
+    if not args.no_extras:
+        t0 = time.perf_counter()
+        extra = extras(dev, max(10, min(args.steps, 50)), dec)
+        torch.cuda.synchronize()
+        busy_s = time.perf_counter() - t0
+
     for _ in range(args.warmup):
         prefill()
         decode()
@@ -408,7 +422,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    pre_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    pre_steps = [e[0].elapsed_time(e[1]) for e in ev]
+    pre_ms = sorted(pre_steps)
     dec_ms = sorted(e[2].elapsed_time(e[3]) for e in ev)
     pre_avg = sum(pre_ms) / K
     dec_avg = sum(dec_ms) / K
@@ -446,7 +461,8 @@ def main():
                        "split_tokens": split, "bytes": dec_bytes},
         },
         "prefill": {"value": round(tflops, 3), "unit": "TFLOP/s", "kernel_ms": round(pre_avg, 5),
-                    "kernel_ms_median": round(pre_ms[K // 2], 5), "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4)},
+                    "kernel_ms_median": round(pre_ms[K // 2], 5), "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                    "kernel_ms_by_step": [round(x, 4) for x in pre_steps]},
         "decode": {"value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(dec_avg, 5),
                    "kernel_ms_median": round(dec_ms[K // 2], 5), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -458,8 +474,10 @@ def main():
                             "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
         "wall_s_timed": round(wall, 4),
     }
-    if not args.no_extras:
-        out["extras"] = extras(dev, max(10, min(K, 50)), dec)
+    out["preconditioning"] = {"extras_first": extra is not None, "gpu_busy_s_before_warmup": round(busy_s, 2),
+                              "warmup_steps": args.warmup}
+    if extra is not None:
+        out["extras"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -409,31 +409,48 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
+// One wave per (sequence, query head): the lanes first share out the split
+// log-sum-exps (max, then weights and their sum, reduced across the wave),
+// then each lane sums its d/64 output elements over the splits with
+// independent loads.  Four (sequence, head) rows per workgroup.
+constexpr int kMergeRows = 4;
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kMergeRows) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int E = D / 64;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * kMergeRows + (threadIdx.x >> 6);
+  if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq;
   const int ns = key_range(a.seq_lens[b], a).ns;
   if (ns == 1) return;  // written by the split kernel
   const size_t slot0 = (size_t)bh * a.max_splits;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[slot0 + s]);
-  const int e = threadIdx.x;
-  float wsum = 0.f, acc = 0.f;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.ws_lse[slot0 + s]);
+  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+  float wsum = 0.f;
+  for (int s = lane; s < ns; s += 64) wsum += __expf(a.ws_lse[slot0 + s] - M);
+  for (int x = 32; x >= 1; x >>= 1) wsum += __shfl_xor(wsum, x);
+  float acc[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) acc[j] = 0.f;
+  const float* wo = a.ws_o + slot0 * D + lane * E;
+#pragma unroll 4
   for (int s = 0; s < ns; ++s) {
     const float w = __expf(a.ws_lse[slot0 + s] - M);
-    wsum += w;
-    if (e < a.d) acc = fmaf(w, a.ws_o[(slot0 + s) * a.d + e], acc);
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc[j] = fmaf(w, wo[(size_t)s * D + j], acc[j]);
   }
-  if (e < a.d) {
-    const float out = acc / wsum;
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const float out = acc[j] * inv;
     if constexpr (sizeof(T) == 4) {
-      reinterpret_cast<float*>(a.o)[(size_t)bh * a.d + e] = out;
+      reinterpret_cast<float*>(a.o)[(size_t)bh * D + lane * E + j] = out;
     } else {
-      reinterpret_cast<uint16_t*>(a.o)[(size_t)bh * a.d + e] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
+      reinterpret_cast<uint16_t*>(a.o)[(size_t)bh * D + lane * E + j] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
     }
   }
-  if (a.lse && e == 0) a.lse[bh] = M + __logf(wsum);
+  if (a.lse && lane == 0) a.lse[bh] = M + __logf(wsum);
 }
 
 template <typename T, int D, int QH>
@@ -446,7 +463,8 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_split_kernel<T, D, QH, false>), grid, dim3(kWaves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3(a.B * a.Hq), dim3(128), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((a.B * a.Hq + kMergeRows - 1) / kMergeRows), dim3(64 * kMergeRows),
+                     0, st, a);
   return hipGetLastError();
 }
 

@@ -185,23 +185,110 @@ struct PagedCopy {
   }
 };
 
+// Key tiles that query tile qb of sequence b visits (the key range run_tile
+// computes): with a cache (seq_lens) the sequences differ in length.
+__device__ __forceinline__ int tile_count(const PrefillArgs& a, int W, int b, int qb) {
+  const int L = a.seq_lens[b];
+  if (L < 0 || L > a.max_seq_len || (a.causal && L < a.Nq)) return 0;
+  const int off = L - a.Nq, q0 = qb * kBM, last = min(a.Nq, q0 + kBM) - 1;
+  const int kend = a.causal ? min(L, last + off + 1) : L;
+  const int tb = (W > 0 ? max(0, q0 + off - W + 1) : 0) / kBN;
+  return max(tb, (kend + kBN - 1) / kBN) - tb;
+}
+
+// Longest-first work list of a launch over sequences of different lengths:
+// the (sequence, query tile) item of rank r when the B * nqb items are ordered
+// by key-tile count, longest first, ties by item index (b * nqb + qb).  Every
+// workgroup computes the same order (a histogram of the counts, an exclusive
+// prefix over it, then a stable selection inside the bucket of rank r), so
+// the workgroups of a launch take every item exactly once.  `scratch` holds
+// kLptBuckets + 8 words of LDS; all threads of the workgroup call this.
+constexpr int kLptBuckets = 1024;  // counts past the last bucket share it (ordered by index)
+__device__ int lpt_item(const PrefillArgs& a, int W, int nqb, int r, uint32_t* scratch) {
+  uint32_t* hist = scratch;                  // bucket 0 = the most key tiles
+  uint32_t* wsum = scratch + kLptBuckets;    // per-wave totals of a scan (8)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = a.B * nqb;
+  auto bucket = [&](int i) { return kLptBuckets - 1 - min(tile_count(a, W, i / nqb, i % nqb), kLptBuckets - 1); };
+  for (int i = tid; i < kLptBuckets; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kThreads) atomicAdd(&hist[bucket(i)], 1u);
+  __syncthreads();
+  // exclusive prefix over the buckets, two per thread: the bucket holding rank r
+  static_assert(kLptBuckets == 2 * kThreads, "two buckets per thread");
+  const uint32_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+  uint32_t incl = h0 + h1;
+  for (int x = 1; x < 64; x <<= 1) {
+    const uint32_t y = __shfl_up(incl, x, 64);
+    if (lane >= x) incl += y;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  uint32_t start = incl - h0 - h1;
+  for (int w = 0; w < wv; ++w) start += wsum[w];
+  __syncthreads();  // every wave has read wsum
+  int kb = -1;
+  uint32_t target = 0;
+  if ((uint32_t)r >= start && (uint32_t)r < start + h0) { kb = 2 * tid; target = r - start; }
+  if ((uint32_t)r >= start + h0 && (uint32_t)r < start + h0 + h1) { kb = 2 * tid + 1; target = r - start - h0; }
+  if (kb >= 0) { wsum[0] = kb; wsum[1] = target; }
+  __syncthreads();
+  const int k = (int)wsum[0];
+  const uint32_t tgt = wsum[1];
+  __syncthreads();
+  // the tgt-th item of bucket k in index order
+  uint32_t seen = 0;
+  for (int c0 = 0; c0 < n; c0 += kThreads) {
+    const int i = c0 + tid;
+    const bool f = i < n && bucket(i) == k;
+    const unsigned long long m = __ballot(f);
+    if (lane == 0) wsum[wv] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t before = seen;
+    for (int w = 0; w < wv; ++w) before += wsum[w];
+    uint32_t total = 0;
+    for (int w = 0; w < kThreads / 64; ++w) total += wsum[w];
+    const uint32_t mine = before + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    __syncthreads();  // every wave has read wsum
+    if (f && mine == tgt) wsum[8 - 1] = i;  // slot 7: read after the next barrier
+    __syncthreads();
+    seen += total;
+    if (seen > tgt) break;
+  }
+  const int item = (int)wsum[7];
+  __syncthreads();  // the scratch may be overwritten after this
+  return item;
+}
+
 template <int D, bool PAGED, bool WINDOW>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a, int nqb) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a, int nqb, int lpt) {
   __shared__ Smem<D> sm;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int VPS = 16 / KS; // softmax values of one 32-key block per QK^T k-step
 
-  // ---- work item: (b, h, pair of query tiles), KV-head-major per XCD.
-  // A workgroup takes query tiles nqb - 1 - pr and pr of one head: with a
+  // ---- work item.  Sequences of one length (plain prefill, or a single
+  // cached sequence): (b, h, pair of query tiles), KV-head-major per XCD.  A
+  // workgroup takes query tiles nqb - 1 - pr and pr of one head: with a
   // causal mask their key-tile counts add up to the same total for every
   // pair, so all workgroups carry equal work (the lone middle tile of an odd
-  // count comes last).
+  // count comes last).  Cached sequences of different lengths (lpt): one
+  // query tile per workgroup, the (sequence, tile) items taken longest first
+  // so that the hardware's in-order dispatch onto free CUs balances them; the
+  // Hq workgroups of an item are consecutive, each XCD getting whole KV-head
+  // groups.
   const int id = blockIdx.x;
   const int n_rep = a.Hq / a.Hkv;
   const int GP = a.B * a.Hkv;
-  int b, h, pr;
-  if ((GP & 7) == 0) {
+  int b, h, pr, single = -1;
+  if (lpt) {
+    const int item = lpt_item(a, WINDOW ? a.window : 0, nqb, id / a.Hq, reinterpret_cast<uint32_t*>(sm.k[0]));
+    const int j = id % a.Hq;
+    b = item / nqb;
+    single = item % nqb;
+    pr = 0;
+    h = (j % a.Hkv) * n_rep + j / a.Hkv;
+  } else if ((GP & 7) == 0) {
     const int xcd = id & 7, j = id >> 3;
     const int per = (GP >> 3) * n_rep;  // work items per pair rank on one XCD
     const int rest = j % per;
@@ -648,17 +735,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         w[1] = pack_bf16x2(oacc[db][q4 * 4 + 2] * inv, oacc[db][q4 * 4 + 3] * inv);
         *reinterpret_cast<u32x2_t*>(ot + ecol * D + (((db * 4 + q4) ^ k_swz<D>(ecol)) * 8) + hl * 4) = w;
       }
+    // The output goes out with non-temporal stores: written through, it does
+    // not sit dirty in L2 at the end of the launch (measured on MI355X: ~1%
+    // shorter launches at N = 4096, where the last tile's output is written
+    // right before the kernel ends).
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + q0 + wave * 32) * D;
 #pragma unroll
     for (int i = 0; i < 32 * CPR / 64; ++i) {
       const int u = i * 64 + elane, r = u / CPR, ch = u % CPR;
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + r * D + ((ch ^ k_swz<D>(r)) * 8));
-      if (q0 + wave * 32 + r < a.Nq) *reinterpret_cast<u32x4_t*>(obase + r * D + ch * 8) = val;
+      if (q0 + wave * 32 + r < a.Nq) __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(obase + r * D + ch * 8));
     }
     if (a.lse && hl == 0 && qrow < a.Nq)
       a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
   };
+  if (single >= 0) {
+    run_tile(single);
+    return;
+  }
   run_tile(nqb - 1 - pr);
   if (pr < nqb - 1 - pr) {
     __syncthreads();  // the first tile's last LDS reads are done
@@ -670,11 +765,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.Nq + kBM - 1) / kBM;
-  const long long grid = (long long)((nqb + 1) / 2) * a.Hq * a.B;  // pairs of query tiles
+  // several cached sequences (lengths known only to the device): single query
+  // tiles, longest first; otherwise pairs of query tiles
+  const int lpt = a.seq_lens != nullptr && a.B > 1;
+  const long long grid = (long long)(lpt ? nqb : (nqb + 1) / 2) * a.Hq * a.B;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool paged = a.block_table != nullptr, win = a.window > 0;
 #define FA_LAUNCH(DD, PG, WN) \
-  hipLaunchKernelGGL((prefill_bf16_kernel<DD, PG, WN>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb)
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, PG, WN>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, nqb, lpt)
   if (a.d == 64) {
     if (paged) { if (win) FA_LAUNCH(64, true, true); else FA_LAUNCH(64, true, false); }
     else { if (win) FA_LAUNCH(64, false, true); else FA_LAUNCH(64, false, false); }

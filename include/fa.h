@@ -19,9 +19,11 @@
  *     safe to call from several host threads.
  *   - Outputs are deterministic: the same inputs and launch configuration give
  *     the same bits.  No kernel accumulates a result with atomics; the only
- *     atomics are the LDS counters with which fa_mla_decode's planning step
- *     orders its work list, and they decide only which workgroup runs which
- *     split, never a value that is written.
+ *     atomics are LDS counters that build a histogram from which a work list
+ *     is ordered (fa_mla_decode's planning step, and fa_chunked_prefill over
+ *     several sequences): the counts are exact, so the order is the same on
+ *     every run, and it decides only which workgroup computes which part,
+ *     never a value that is written.
  */
 #ifndef FA_H
 #define FA_H

@@ -150,6 +150,35 @@ def test_chunked_prefill_small(fa, case, dt):
     check(o, lse, O_ref, lse_ref, dt, f"chunked {case}")
 
 
+@pytest.mark.parametrize("paged", [True, False], ids=["paged", "contig"])
+def test_chunked_prefill_many_sequences_longest_first(fa, paged):
+    """Several cached sequences run one query tile per workgroup, taken
+    longest first from a work list every workgroup computes alike.  640
+    (sequence, tile) items (more than one 512-item pass of the selection),
+    lengths with many ties, and two sequences that break the contract (their
+    rows must come out NaN): every item is computed exactly once."""
+    B, Hq, Hkv, d, n = 160, 2, 1, 64, 1000
+    g = np.random.default_rng(51)
+    past = [int(x) for x in g.integers(0, 300, B)]
+    ci = W.make_chunked_inputs(B, Hq, Hkv, d, "bf16", seed=51, chunk=n, past_lens=past, paged=paged,
+                               block_size=16, s_cap=(max(past) + n + 5) if not paged else None)
+    kc, vc, lens, table = gpu_append(fa, ci)
+    bad = lens.clone()
+    bad[7] = n - 1                      # causal chunk longer than the cached sequence
+    bad[90] = ci.max_seq_len + 1        # longer than max_seq_len
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.chunked_prefill(ci.q.to(DEV), kc, vc, bad, block_table=table, max_seq_len=ci.max_seq_len,
+                                scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isnan(o[7].float()).all() and torch.isnan(o[90].float()).all()
+    assert torch.isnan(lse[7]).all() and torch.isnan(lse[90]).all()
+    keep = [b for b in range(B) if b not in (7, 90)]
+    kr, vr = oracle_append(ci)
+    O_ref, lse_ref = oracle.chunked_prefill(ci.q, kr, vr, ci.seq_lens, scale, True, ci.block_table, ci.block_size)
+    check(o[keep], lse[keep], O_ref[keep], lse_ref[keep], "bf16", "many sequences")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_chunked_prefill_without_past_is_prefill_bit_for_bit(fa, dt, d):
