@@ -126,12 +126,30 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+class Prepared:
+    """One library call with its arguments checked and marshalled once
+    (pointers, sizes and the stream fixed): calling it only enqueues the
+    kernels again, for loops that repeat the same call on the same buffers."""
+
+    def __init__(self, name: str, args, keep):
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._keep = keep  # the tensors the pointers refer to stay alive
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, want_lse: bool = True, window: int = 0,
-            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            stream=None, prepare: bool = False):
     """fa_prefill: q (B, Hq, Nq, d), k/v (B, Hkv, Nk, d) -> (o, lse).
-    ``window`` > 0: causal sliding window of that many keys."""
+    ``window`` > 0: causal sliding window of that many keys.  With
+    ``prepare``, nothing is launched: returns (call, o, lse), where call()
+    enqueues this prefill on the given (or current) stream."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -144,9 +162,11 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
         scale = 1.0 / math.sqrt(d)
     out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
     lse = _lse_tensor(lse, want_lse, (B, Hq, Nq), q.device)
-    _check(lib().fa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                            B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window), float(scale),
-                            _dtype_code(q), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window),
+            float(scale), _dtype_code(q), _stream(stream))
+    if prepare:
+        return Prepared("fa_prefill", args, (q, k, v, out, lse)), out, lse
+    _check(lib().fa_prefill(*args))
     return out, lse
 
 
@@ -301,12 +321,13 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
            max_seq_len: Optional[int] = None, scale: Optional[float] = None,
            split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           want_lse: bool = True, window: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+           want_lse: bool = True, window: int = 0, stream=None, prepare: bool = False):
     """fa_decode: q (B, Hq, d) against a contiguous cache (B, Hkv, S_cap, d) or,
     with ``block_table`` (B, max_blocks) int32, a paged pool
     (num_blocks, block_size, Hkv, d).  ``max_seq_len`` bounds seq_lens; it
     defaults to the capacity of the layout (no device read-back).  ``window``
-    > 0 attends only the last ``window`` keys."""
+    > 0 attends only the last ``window`` keys.  ``prepare``: as for
+    ``prefill``, returns (call, o, lse) without launching."""
     B, Hq, d = q.shape
     c = _cache_layout(q, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
     Hkv, paged, block_size, capacity, max_blocks = c.Hkv, c.paged, c.block_size, c.capacity, c.max_blocks
@@ -320,11 +341,13 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
     out = _out_tensor(out, q.shape, q.dtype, q.device, "out")
     lse = _lse_tensor(lse, want_lse, (B, Hq), q.device)
     ws_bytes = _workspace_bytes(workspace, q.device)
-    _check(lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
-                           block_size if paged else 0, max_blocks, capacity, int(max_seq_len), int(window),
-                           _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
-                           int(split_tokens), _ptr(workspace) if need else None, ws_bytes,
-                           _stream(stream)))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+            block_size if paged else 0, max_blocks, capacity, int(max_seq_len), int(window),
+            _ptr(out), _ptr(lse), B, Hq, Hkv, d, float(scale), _dtype_code(q),
+            int(split_tokens), _ptr(workspace) if need else None, ws_bytes, _stream(stream))
+    if prepare:
+        return Prepared("fa_decode", args, (q, k_cache, v_cache, seq_lens, block_table, out, lse, workspace)), out, lse
+    _check(lib().fa_decode(*args))
     return out, lse
 
 

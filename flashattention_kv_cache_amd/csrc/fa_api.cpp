@@ -445,7 +445,9 @@ size_t fa_mla_decode_workspace_bytes(int B, int Hq, int d_c, int d_r, int max_se
   const int ns = max_splits_for(max_seq_len, st);
   if (ns <= 1) return 0;
   const size_t slots = (size_t)B * Hq * ns;
-  const size_t o_bytes = (slots * d_c * sizeof(float) + 255) & ~(size_t)255;
+  // bf16 partial outputs (they are normalised, and the output itself is bf16),
+  // fp32 log-sum-exps, then the work list
+  const size_t o_bytes = (slots * d_c * sizeof(uint16_t) + 255) & ~(size_t)255;
   const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
   const size_t p_bytes = ((1 + (size_t)B * ns) * sizeof(int32_t) + 255) & ~(size_t)255;
   return o_bytes + l_bytes + p_bytes;
@@ -487,9 +489,9 @@ int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, 
   a.split_tokens = stoks; a.max_splits = ns;
   if (ns > 1) {
     const size_t slots = (size_t)B * Hq * ns;
-    const size_t o_bytes = (slots * d_c * sizeof(float) + 255) & ~(size_t)255;
+    const size_t o_bytes = (slots * d_c * sizeof(uint16_t) + 255) & ~(size_t)255;
     const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
-    a.ws_o = reinterpret_cast<float*>(workspace);
+    a.ws_o = reinterpret_cast<uint16_t*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
     a.plan = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + o_bytes + l_bytes);
   }

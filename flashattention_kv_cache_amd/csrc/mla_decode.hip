@@ -38,7 +38,9 @@
 //   * the streaming softmax (running max with a lazy rescale, fp32 row sum of
 //     the unrounded weights, bf16 weights into PV) is the prefill kernel's;
 //   * splits of a sequence write (output, log-sum-exp) partials that a merge
-//     kernel combines with weights exp(lse_s - max lse).
+//     kernel combines with weights exp(lse_s - max lse); the normalised
+//     partial outputs are stored in bf16 (the output's own precision), their
+//     log-sum-exps in fp32.
 #include "fa_internal.h"
 
 namespace fa {
@@ -457,10 +459,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
     }
     if (a.lse && g == 0) a.lse[(size_t)b * a.Hq + h] = lse;
   } else {
+    // the partial output in bf16 (normalised: within bf16 rounding of the
+    // final output, which is bf16 too), its log-sum-exp in fp32: half the
+    // partials' round trip through memory
     const size_t slot = ((size_t)b * a.Hq + h) * a.max_splits + s;
-    float* op = a.ws_o + slot * kDC + 4 * g;
+    uint16_t* op = a.ws_o + slot * kDC + 4 * g;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = oacc[db] * inv;
+    for (int db = 0; db < kDB; ++db) {
+      u32x2_t w2;
+      w2[0] = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
+      w2[1] = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
+      *reinterpret_cast<u32x2_t*>(op + 16 * db) = w2;
+    }
     if (g == 0) a.ws_lse[slot] = lse;
   }
 }
@@ -483,7 +493,11 @@ __global__ __launch_bounds__(kDC / 4) void mla_merge_kernel(MlaArgs a) {
   for (int s = 0; s < ns; ++s) {
     const float w = __expf(a.ws_lse[slot0 + s] - M);
     wsum += w;
-    acc += w * *reinterpret_cast<const f32x4*>(a.ws_o + (slot0 + s) * kDC + e);
+    const u32x2_t p = *reinterpret_cast<const u32x2_t*>(a.ws_o + (slot0 + s) * kDC + e);
+    acc[0] = fmaf(w, bf16lo_to_f32(p[0]), acc[0]);
+    acc[1] = fmaf(w, bf16hi_to_f32(p[0]), acc[1]);
+    acc[2] = fmaf(w, bf16lo_to_f32(p[1]), acc[2]);
+    acc[3] = fmaf(w, bf16hi_to_f32(p[1]), acc[3]);
   }
   const float inv = 1.f / wsum;
   u32x2_t out;

@@ -315,8 +315,8 @@ int fa_mla_decode(const void* q, const void* kv_cache, const int32_t* seq_lens, 
 int fa_mla_decode_split_tokens(int B, int Hq, int d_c, int d_r, int max_seq_len);
 
 /* Workspace bytes fa_mla_decode needs (0 when every sequence fits in one split or the sizes are rejected):
- * the split partials (B x Hq x splits x d_c fp32, then their log-sum-exps) and a
- * work list (1 + B x splits int32) that orders the splits longest first. */
+ * the split partials (B x Hq x splits x d_c bf16, then their fp32 log-sum-exps)
+ * and a work list (1 + B x splits int32) that orders the splits longest first. */
 size_t fa_mla_decode_workspace_bytes(int B, int Hq, int d_c, int d_r, int max_seq_len, int split_tokens);
 
 /*

@@ -22,6 +22,7 @@ class _NoLibrary:
 def cpu_binding(monkeypatch):
     monkeypatch.setattr(binding, "_dev", lambda t, n: None)
     monkeypatch.setattr(binding, "lib", lambda: _NoLibrary())
+    monkeypatch.setattr(binding, "_stream", lambda stream: None)  # no device to ask for its stream
     # the workspace size is a library query: answer it without the library
     monkeypatch.setattr(binding, "decode_workspace_bytes", lambda *a, **k: 0)
     monkeypatch.setattr(binding, "mla_decode_workspace_bytes", lambda *a, **k: 0)

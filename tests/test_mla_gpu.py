@@ -163,7 +163,8 @@ def test_mla_work_list_orders_every_split_longest_first(fa, st):
     torch.cuda.synchronize()
     items, ns = _expected_items(lens.tolist(), max_len, st)
     slots = B * Hq * ns
-    off = -(-slots * 512 * 4 // 256) * 256 + -(-slots * 4 // 256) * 256
+    # workspace: bf16 partial outputs, fp32 partial LSEs, then the plan (each 256-byte aligned)
+    off = -(-slots * 512 * 2 // 256) * 256 + -(-slots * 4 // 256) * 256
     plan = ws[off:off + 4 * (1 + len(items))].cpu().view(torch.int32).tolist()
     assert plan[0] == len(items)
     order = plan[1:]
