@@ -189,13 +189,26 @@ __device__ __forceinline__ void pin(const u32x4_t& x) { asm volatile("" ::"v"(x)
 // vector-memory loads retire in order, so the compiler's own waits for other
 // loads stay correct (only stricter).  M0 is written in the same block and
 // declared clobbered; s_nop 0 covers the M0-write -> LDS-DMA hazard.
+//
+// NT = true sets the non-temporal bit: for data read once per launch (a KV
+// cache streamed by decode), which then does not displace reusable lines in L2.
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma_saddr(uint32_t voff, const void* sbase, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma_vaddr(const void* vaddr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(vaddr), "s"(lds_addr) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(vaddr), "s"(lds_addr) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(vaddr), "s"(lds_addr) : "memory", "m0");
 }
 
 

@@ -22,7 +22,8 @@
 //     32 keys).  Sixteen heads per wave keep the wave within 256 registers;
 //     32 would need 256 accumulators alone;
 //   * 32-key tiles of cache rows go HBM -> LDS with global_load_lds_dwordx4,
-//     one tile serves both products (V is a prefix of K);
+//     one tile serves both products (V is a prefix of K); the loads carry the
+//     non-temporal bit, since each row is read once per call;
 //   * rows are 72 sixteen-byte units; unit u of row r sits at u ^ (r % 8)
 //     (low three bits only).  Measured with the LDS bank-conflict counter on
 //     MI355X, this keeps both the K operand reads (16 rows at one unit) and
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
         } else {
           base = kv + ((size_t)b * a.kv_capacity + tok0) * kDK;
         }
-        lds_dma_saddr(dma_off[k], base, lds0 + i * 1024);
+        lds_dma_saddr<true>(dma_off[k], base, lds0 + i * 1024);
       }
     } else {
       // each lane finds its own token; rows past the split read its last
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_split_kernel(MlaArgs a) {
         } else {
           row = (size_t)b * a.kv_capacity + tok;
         }
-        lds_dma_vaddr(kv + row * kDK + lu * 8, lds0 + i * 1024);
+        lds_dma_vaddr<true>(kv + row * kDK + lu * 8, lds0 + i * 1024);
       }
     }
   };
