@@ -24,6 +24,7 @@ against a contiguous cache, and MLA decode, each on its own.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -112,17 +113,39 @@ def time_launches(fn, steps: int, warmup: int, back_to_back: bool = False):
 
 
 def extras(dev, steps: int, dec):
-    """Measurements outside the step, each kernel on its own:
+    """Measurements outside the step, each kernel on its own, in this order:
+      * causal GQA prefill at N = 32768 with 64 query heads;
       * the KV append and the chunked prefill against a paged cache: 1024-token
         chunks of 4 sequences appended to paged caches holding 1024..7168
         tokens, then attended causally against the whole sequences;
       * sliding-window attention (W = 4096): a causal GQA prefill of 32768
-        tokens, and the resident paged decode batch with the window applied.
+        tokens, and the resident paged decode batch with the window applied;
+      * the resident paged decode batch against an FP8 (E4M3) copy of its cache;
+      * decode against a contiguous cache (64 sequences of 1024..8192 tokens);
+      * MLA decode (absorbed latent form), last: it runs right before the
+        step's warm-up, with nothing freed or computed on the host after it.
     ``dec`` holds the decode batch already in HBM."""
     import torch
     from flashattention_kv_cache_amd import binding
     from flashattention_kv_cache_amd import workloads as W
     out = {}
+    # long-context causal GQA prefill (N = 32768, 64 query heads), first: after
+    # this much MFMA load the clocks take a while to recover, which the decode
+    # kernels measured right after it would pay for (measured on MI355X: the
+    # contiguous decode batch 8% slower)
+    w4 = W.C4
+    q, k, v = (t.to(dev) for t in W.prefill_inputs(w4))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    p_avg, p_med = time_launches(lambda: binding.prefill(q, k, v, causal=True, scale=w4.scale, out=o, lse=lse),
+                                 max(5, steps // 5), 3)
+    tf = w4.flops() / (p_avg * 1e-3) / 1e12
+    out["prefill_long"] = {"workload": w4.name, "value": round(tf, 3), "unit": "TFLOP/s", "kernel_ms": round(p_avg, 5),
+                           "kernel_ms_median": round(p_med, 5), "flops": w4.flops(),
+                           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                        "kernel": "prefill_bf16_kernel<128, contiguous, no window>"}}
+    del q, k, v, o, lse
     w = W.CHUNKED
     ci = W.chunked_inputs(w)
     q, kn, vn = ci.q.to(dev), ci.k_new.to(dev), ci.v_new.to(dev)
@@ -131,8 +154,9 @@ def extras(dev, steps: int, dec):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
 
-    def append():
-        binding.kv_append(kn, vn, kc, vc, lens, block_table=table)
+    # checked and marshalled once: a launch then costs the host a few
+    # microseconds, less than the kernel, so back-to-back launches time the GPU
+    append = binding.kv_append(kn, vn, kc, vc, lens, block_table=table, prepare=True)
 
     def chunk():
         binding.chunked_prefill(q, kc, vc, lens, block_table=table, max_seq_len=ci.max_seq_len,
@@ -164,7 +188,7 @@ def extras(dev, steps: int, dec):
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "kv_append_kernel"}},
     })
-    del q, kn, vn, kc, vc, o, lse
+    del q, kn, vn, kc, vc, o, lse, ci
 
     # sliding window: prefill
     wp = W.WINDOW_PREFILL
@@ -234,22 +258,7 @@ def extras(dev, steps: int, dec):
                                       "kernel": "decode_split_kernel<fp8,128,4,paged> + decode_merge_kernel"}}
     del fk, fv
 
-    # the two configurations of the hot path outside the step, each on its own:
-    # long-context causal GQA prefill (N = 32768, 64 query heads) ...
-    w4 = W.C4
-    q, k, v = (t.to(dev) for t in W.prefill_inputs(w4))
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    p_avg, p_med = time_launches(lambda: binding.prefill(q, k, v, causal=True, scale=w4.scale, out=o, lse=lse),
-                                 max(5, steps // 5), 3)
-    tf = w4.flops() / (p_avg * 1e-3) / 1e12
-    out["prefill_long"] = {"workload": w4.name, "value": round(tf, 3), "unit": "TFLOP/s", "kernel_ms": round(p_avg, 5),
-                           "kernel_ms_median": round(p_med, 5), "flops": w4.flops(),
-                           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
-                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                        "kernel": "prefill_bf16_kernel<128, contiguous, no window>"}}
-    del q, k, v, o, lse
-    # ... and decode against a contiguous cache (64 sequences, S_cap 8192)
+    # decode against a contiguous cache (64 sequences, S_cap 8192)
     w3 = W.C3
     di = W.decode_inputs(w3)
     cq, ck, cv, cl = di.q.to(dev), di.k_cache.to(dev), di.v_cache.to(dev), di.seq_lens.to(dev)
@@ -277,15 +286,23 @@ def extras(dev, steps: int, dec):
     ml, mt = mi.seq_lens.to(dev), mi.block_table.to(dev)
     mo = torch.empty((wm.B, wm.Hq, wm.d_c), dtype=torch.bfloat16, device=dev)
     mlse = torch.empty((wm.B, wm.Hq), dtype=torch.float32, device=dev)
-    st = binding.mla_decode_split_tokens(wm.B, wm.Hq, mi.max_seq_len)
-    ws = torch.empty(max(1, binding.mla_decode_workspace_bytes(wm.B, wm.Hq, mi.max_seq_len, st)),
+    mmax = mi.max_seq_len
+    st = binding.mla_decode_split_tokens(wm.B, wm.Hq, mmax)
+    ws = torch.empty(max(1, binding.mla_decode_workspace_bytes(wm.B, wm.Hq, mmax, st)),
                      dtype=torch.uint8, device=dev)
-    m_avg, m_med = time_launches(lambda: binding.mla_decode(mq, mkv, ml, wm.scale, block_table=mt,
-                                                            max_seq_len=mi.max_seq_len, split_tokens=st,
-                                                            workspace=ws, out=mo, lse=mlse), steps, 20)
     mflops = wm.flops(mi.seq_lens.tolist())
     mbytes = mi.kv_bytes() + mq.numel() * 2 + mo.numel() * 2 + mlse.numel() * 4 + \
         int(((mi.seq_lens.to(torch.int64) + wm.block_size - 1) // wm.block_size).sum()) * 4 + wm.B * 4
+    # This is the last kernel before the step's warm-up: the host copies of its
+    # inputs (1.3 GB) are freed before it is timed, not after, since freeing
+    # them takes tens of milliseconds, and an idle GPU of that length before the
+    # warm-up makes the first ~15 timed steps run up to 30% slower while the
+    # clocks recover (measured on MI355X).
+    del mi
+    gc.collect()
+    m_avg, m_med = time_launches(lambda: binding.mla_decode(mq, mkv, ml, wm.scale, block_table=mt,
+                                                            max_seq_len=mmax, split_tokens=st,
+                                                            workspace=ws, out=mo, lse=mlse), steps, 20)
     tf = mflops / (m_avg * 1e-3) / 1e12
     gbs = mbytes / (m_avg * 1e-3) / 1e9
     out["mla_decode"] = {"workload": wm.name, "value": round(tf, 3), "unit": "TFLOP/s", "kernel_ms": round(m_avg, 5),
@@ -385,11 +402,13 @@ def main():
     decode = binding.decode(dq, dk, dv, dl, block_table=dt_, max_seq_len=wd.len_hi, scale=wd.scale,
                             split_tokens=split, workspace=ws, out=do, lse=dlse, prepare=True)[0]
 
-    # The measurements outside the step run first: they keep the GPU busy for
-    # a second or more, so the timed steps see the clocks a GPU under
-    # continuous load holds (after a few milliseconds of idle-to-busy, prefill
-    # launches run up to 30% slower for the first ~20 steps while the clocks
-    # settle).  With --no-extras, the W warm-up steps are all the warm-up.
+    # The measurements outside the step run first and end right before the
+    # warm-up: they keep the GPU busy for two seconds, so the timed steps see
+    # the clocks a GPU under continuous load holds.  Measured on MI355X: after
+    # an idle gap of 30 ms or more, the prefill launches of the next ~15 steps
+    # run up to 30% slower while the clocks recover (5% on the average of 20
+    # steps); straight from other work they run at the steady rate from the
+    # first step.  With --no-extras, the W warm-up steps are all the warm-up.
     extra = None
     busy_s = 0.0
     if not args.no_extras:

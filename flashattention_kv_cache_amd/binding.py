@@ -264,10 +264,11 @@ def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tenso
 
 def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None, block_size: int = 0,
-              stream=None) -> None:
+              stream=None, prepare: bool = False):
     """fa_kv_append: write k_new/v_new (B, Hkv, n_new, d) into the cache at
     positions seq_lens[b] - n_new .. seq_lens[b] - 1 (seq_lens = lengths after
-    the append), in place."""
+    the append), in place.  With ``prepare``, nothing is launched: returns a
+    call that enqueues this append."""
     _dev(v_new, "v_new")
     if k_new.dim() != 4 or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
         raise ValueError("expected k_new, v_new (B, Hkv, n_new, d) of one dtype")
@@ -275,9 +276,11 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v
     c = _cache_layout(k_new, k_cache, v_cache, seq_lens, block_table, block_size, B, d)
     if c.Hkv != Hkv:
         raise ValueError("new rows and cache disagree in KV heads")
-    _check(lib().fa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
-                              _ptr(block_table), c.block_size, c.max_blocks, c.capacity,
-                              B, Hkv, n_new, d, _dtype_code(k_new), _stream(stream)))
+    args = (_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+            c.block_size, c.max_blocks, c.capacity, B, Hkv, n_new, d, _dtype_code(k_new), _stream(stream))
+    if prepare:
+        return Prepared("fa_kv_append", args, (k_new, v_new, k_cache, v_cache, seq_lens, block_table))
+    _check(lib().fa_kv_append(*args))
 
 
 def chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
