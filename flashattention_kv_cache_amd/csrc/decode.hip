@@ -33,8 +33,11 @@
 //     Hongyi, Machine Learning 2026" notes, lecture "FlashAttention" — so the
 //     loop has no cross-group traffic; the groups, then the four waves, are
 //     combined once at the end;
+//   * when a sequence spans several splits, a one-workgroup kernel first
+//     lists the (sequence, split) work items longest first, and the split
+//     kernel's workgroups take them in that order;
 //   * the partial (normalised output, log-sum-exp) of each split goes to the
-//     workspace and a second kernel merges a sequence's splits with weights
+//     workspace and a last kernel merges a sequence's splits with weights
 //     exp(lse_s - max lse) — the same recurrence applied to whole splits.  A
 //     sequence that fits in one split is written directly.
 #include <type_traits>
@@ -164,6 +167,41 @@ __device__ __forceinline__ void combine(float& m, float& l, float* o, float m2, 
   m = mn;
 }
 
+// One workgroup: the (sequence, split) work items sorted by length, longest
+// first, into a.plan (a counting sort over 64-token buckets; the order among
+// equal lengths is free, and no result depends on it).  The split kernel's
+// workgroups take the items in this order and the hardware starts them in
+// order as slots free up, so the short last splits of the sequences run at
+// the end instead of leaving slots idle behind a long one (list scheduling,
+// longest first).  plan[0] = number of items.
+constexpr int kPlanTokens = 64;
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ int cnt[kPlanBuckets];
+  for (int i = threadIdx.x; i < kPlanBuckets; i += kPlanThreads) cnt[i] = 0;
+  __syncthreads();
+  auto bucket = [&](int L, const KeyRange& kr, int s) {
+    if (kr.bad) return 0;
+    const int t0 = kr.kbeg + s * a.split_tokens, t1 = min(L, t0 + a.split_tokens);
+    return min(kPlanBuckets - 1, (t1 - t0 + kPlanTokens - 1) / kPlanTokens);
+  };
+  for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
+    const int L = a.seq_lens[b];
+    const KeyRange kr = key_range(L, a);
+    for (int s = 0; s < kr.ns; ++s) atomicAdd(&cnt[kPlanBuckets - 1 - bucket(L, kr, s)], 1);
+  }
+  __syncthreads();
+  const int total = plan_exclusive_scan(cnt);
+  if (threadIdx.x == 0) a.plan[0] = total;
+  for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
+    const int L = a.seq_lens[b];
+    const KeyRange kr = key_range(L, a);
+    for (int s = 0; s < kr.ns; ++s) {
+      const int pos = atomicAdd(&cnt[kPlanBuckets - 1 - bucket(L, kr, s)], 1);
+      a.plan[1 + pos] = b * a.max_splits + s;
+    }
+  }
+}
+
 template <typename T, int D, int QH, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a) {
   constexpr int G = D / kElems;         // lanes per token row
@@ -178,14 +216,28 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeArgs a)
   __shared__ float red_ml[kWaves][QH][2];
   __shared__ int red_bad[kWaves];
 
-  // grid: x = (KV head, query-head group) fastest, so the workgroups of all
+  // grid: the (KV head, query-head group) fastest, so the workgroups of all
   // heads of one split are dispatched together and read the same pool blocks
-  // (each block interleaves the Hkv heads token by token); y = split; z = b.
-  const int s = blockIdx.y;
+  // (each block interleaves the Hkv heads token by token); then the work item:
+  // with several splits, item i of the longest-first list, else x = heads,
+  // z = b.
   const int nqg = (a.Hq / a.Hkv) / QH;
-  const int g = blockIdx.x / nqg;
-  const int h0 = g * (a.Hq / a.Hkv) + (blockIdx.x % nqg) * QH;
-  const int b = blockIdx.z;
+  int s, b, gx;
+  if (a.plan) {
+    const int ngroups = a.Hkv * nqg;
+    const int idx = blockIdx.x / ngroups;
+    gx = blockIdx.x - idx * ngroups;
+    if (idx >= a.plan[0]) return;
+    const int item = a.plan[1 + idx];
+    b = item / a.max_splits;
+    s = item - b * a.max_splits;
+  } else {
+    gx = blockIdx.x;
+    s = 0;
+    b = blockIdx.z;
+  }
+  const int g = gx / nqg;
+  const int h0 = g * (a.Hq / a.Hkv) + (gx % nqg) * QH;
 
   const int L = a.seq_lens[b];
   const KeyRange kr = key_range(L, a);
@@ -468,7 +520,11 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_merge_kernel(DecodeArg
 template <typename T, int D, int QH>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
   const int nqg = (a.Hq / a.Hkv) / QH;
-  dim3 grid(a.Hkv * nqg, a.max_splits, a.B);
+  dim3 grid(a.Hkv * nqg, 1, a.B);
+  if (a.max_splits > 1) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+    grid = dim3((unsigned)((long long)a.Hkv * nqg * a.B * a.max_splits), 1, 1);
+  }
   if (a.block_table)
     hipLaunchKernelGGL((decode_split_kernel<T, D, QH, true>), grid, dim3(kWaves * 64), 0, st, a);
   else

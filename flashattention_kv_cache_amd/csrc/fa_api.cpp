@@ -144,7 +144,7 @@ int max_splits_for(int max_seq_len, int split_tokens) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 6; }
+int fa_abi_version(void) { return 7; }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
@@ -275,10 +275,12 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len,
   const int ns = max_splits_for(span, st);
   if (ns <= 1) return 0;
   const size_t slots = (size_t)B * Hq * ns;
-  // partial outputs (d floats per slot) then partial LSEs, each 256-byte aligned
+  // partial outputs (d floats per slot), partial LSEs, then the work list of
+  // the (sequence, split) items, each 256-byte aligned
   const size_t o_bytes = (slots * d * sizeof(float) + 255) & ~(size_t)255;
   const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
-  return o_bytes + l_bytes;
+  const size_t p_bytes = ((1 + (size_t)B * ns) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return o_bytes + l_bytes + p_bytes;
 }
 
 }  // extern "C"
@@ -366,8 +368,9 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
       return fail(FA_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID, "workspace must be 256-byte aligned");
   }
-  if (B > 65535 || Hq > 65535 || ns > 65535)
-    return fail(FA_ERR_UNSUPPORTED, "grid too large (B, Hq and the number of splits must be <= 65535)");
+  if (B > 65535 || Hq > 65535 || ns > 65535 || (long long)Hq * B * ns > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (B, Hq and the number of splits must be <= 65535, "
+                "and Hq * B * splits < 2^31)");
   if (static_scratch && need > 0) {  // every argument checked: now the (first-call) address lookup
     const int sc = current_scratch(&workspace);
     if (sc != FA_OK) return sc;
@@ -386,8 +389,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (ns > 1) {
     const size_t slots = (size_t)B * Hq * ns;
     const size_t o_bytes = (slots * d * sizeof(float) + 255) & ~(size_t)255;
+    const size_t l_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = reinterpret_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+    a.plan = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + o_bytes + l_bytes);
   }
   hipError_t e = fa::launch_decode(a, kv, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -62,6 +62,7 @@ struct DecodeArgs {
   int max_splits;     // ceil(max_seq_len / split_tokens), >= 1
   float* ws_o;        // (B, Hq, max_splits, d) partial outputs, when max_splits > 1
   float* ws_lse;      // (B, Hq, max_splits) partial log-sum-exp
+  int32_t* plan;      // 1 + B * max_splits: count, then b * max_splits + s, longest first (max_splits > 1)
 };
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
@@ -154,6 +155,40 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
   bf16x2_t r;
   __builtin_memcpy(&r, &w, sizeof r);
   return r;
+}
+
+// Work lists of the split-K decode kernels: a one-workgroup counting sort of
+// the (sequence, split) items by length, longest first.  The counts sit in
+// kPlanBuckets LDS counters, bucket 0 the longest; this turns them into
+// exclusive start offsets (4 buckets a thread, a scan across lanes, then
+// across waves) and returns the number of items.  All kPlanThreads threads
+// call it; it ends with a barrier.
+constexpr int kPlanThreads = 256, kPlanBuckets = 1024;
+__device__ __forceinline__ int plan_exclusive_scan(int* cnt) {
+  static_assert(kPlanBuckets == 4 * kPlanThreads && kPlanThreads % 64 == 0, "plan scan shape");
+  __shared__ int wave_total[kPlanThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c0 = cnt[4 * t], c1 = cnt[4 * t + 1], c2 = cnt[4 * t + 2], c3 = cnt[4 * t + 3];
+  const int own = c0 + c1 + c2 + c3;
+  int incl = own;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_total[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    if (w < wave) base += wave_total[w];
+    total += wave_total[w];
+  }
+  const int run = base + incl - own;
+  cnt[4 * t] = run;
+  cnt[4 * t + 1] = run + c0;
+  cnt[4 * t + 2] = run + c0 + c1;
+  cnt[4 * t + 3] = run + c0 + c1 + c2;
+  __syncthreads();
+  return total;
 }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum, i.e. not waited).

@@ -128,7 +128,6 @@ __device__ __forceinline__ int split_count(const MlaArgs& a, int L) {
 // One workgroup: the list of work items sorted by tile count, longest first
 // (a counting sort; the order among equal counts is free, and no result
 // depends on it).  plan[0] = number of items.
-constexpr int kPlanThreads = 256, kPlanBuckets = 1024;
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(MlaArgs a) {
   __shared__ int cnt[kPlanBuckets];
   for (int i = threadIdx.x; i < kPlanBuckets; i += kPlanThreads) cnt[i] = 0;
@@ -143,29 +142,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(MlaArgs a) {
     for (int s = 0; s < ns; ++s) atomicAdd(&cnt[kPlanBuckets - 1 - bucket(L, ns, s)], 1);
   }
   __syncthreads();
-  {  // exclusive prefix sum, longest bucket first: 4 buckets a thread, a scan across lanes, then across waves
-    static_assert(kPlanBuckets == 4 * kPlanThreads && kPlanThreads % 64 == 0, "plan scan shape");
-    __shared__ int wave_total[kPlanThreads / 64];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int c0 = cnt[4 * t], c1 = cnt[4 * t + 1], c2 = cnt[4 * t + 2], c3 = cnt[4 * t + 3];
-    const int own = c0 + c1 + c2 + c3;
-    int incl = own;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) wave_total[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wave_total[w];
-    const int run = base + incl - own;
-    cnt[4 * t] = run;
-    cnt[4 * t + 1] = run + c0;
-    cnt[4 * t + 2] = run + c0 + c1;
-    cnt[4 * t + 3] = run + c0 + c1 + c2;
-    if (t == kPlanThreads - 1) a.plan[0] = base + incl;
-  }
-  __syncthreads();
+  const int total = plan_exclusive_scan(cnt);
+  if (threadIdx.x == 0) a.plan[0] = total;
   for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
     const int L = a.seq_lens[b], ns = split_count(a, L);
     for (int s = 0; s < ns; ++s) {

@@ -20,10 +20,11 @@
  *   - Outputs are deterministic: the same inputs and launch configuration give
  *     the same bits.  No kernel accumulates a result with atomics; the only
  *     atomics are LDS counters that build a histogram from which a work list
- *     is ordered (fa_mla_decode's planning step, and fa_chunked_prefill over
- *     several sequences): the counts are exact, so the order is the same on
- *     every run, and it decides only which workgroup computes which part,
- *     never a value that is written.
+ *     is ordered (the planning step of fa_decode, fa_decode_fp8 and
+ *     fa_mla_decode when a sequence spans several splits, and
+ *     fa_chunked_prefill over several sequences): the order among equal
+ *     lengths may differ between runs, but it decides only which workgroup
+ *     computes which part, never a value that is written.
  */
 #ifndef FA_H
 #define FA_H
@@ -47,7 +48,7 @@ typedef enum fa_dtype {
   FA_BF16 = 1  /* bf16 in, bf16 out (round to nearest even), fp32 accumulate */
 } fa_dtype;
 
-/* Version of this ABI (bumped on any signature change). */
+/* Version of this ABI (bumped on any change of a signature or of a workspace size). */
 int fa_abi_version(void);
 
 /* Static description of a status code. */
@@ -104,9 +105,11 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_decode_workspace_bytes — bytes of device workspace fa_decode needs for
- * these sizes (0 when every sequence fits in one split).  `window` and
- * `split_tokens` are the values that will be passed to fa_decode (0 = no
- * window / library choice).  Returns 0 for arguments fa_decode would reject.
+ * these sizes (0 when every sequence fits in one split): the splits' partial
+ * outputs and log-sum-exps, and the list of (sequence, split) work items that
+ * a first small kernel orders longest first.  `window` and `split_tokens` are
+ * the values that will be passed to fa_decode (0 = no window / library
+ * choice).  Returns 0 for arguments fa_decode would reject.
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seq_len, int window,
                                  int split_tokens);

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(fa):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(fa.SIGNATURES) == set(declared_functions())
-    assert L.fa_abi_version() == 6
+    assert L.fa_abi_version() == 7
 
 
 def test_status_strings(fa):
@@ -122,7 +122,9 @@ def test_decode_workspace_contract(fa):
     assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 256, 0, 256) == 0
     n = L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 0, 256)
     slots = 2 * 8 * 4
-    assert n == ((slots * 128 * 4 + 255) // 256) * 256 + ((slots * 4 + 255) // 256) * 256
+    # partial outputs, partial LSEs, then the work list (count + one entry per (sequence, split))
+    assert n == ((slots * 128 * 4 + 255) // 256) * 256 + ((slots * 4 + 255) // 256) * 256 + \
+        ((1 + 2 * 4) * 4 + 255) // 256 * 256
     # a call that needs it without one, or with too little, is rejected
     assert decode(fa, maxlen=1024, cap=1024, split=256) == FA_ERR_INVALID
     assert "workspace" in L.fa_last_error().decode()
@@ -134,7 +136,7 @@ def test_decode_workspace_contract(fa):
     # a window caps the keys a query sees, and with them the splits
     assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 256, 256) == 0
     assert L.fa_decode_workspace_bytes(2, 8, 2, 128, 1024, 512, 256) == \
-        ((2 * 8 * 2 * 128 * 4 + 255) // 256) * 256 + 256
+        ((2 * 8 * 2 * 128 * 4 + 255) // 256) * 256 + 256 + 256
 
 
 def test_decode_split_choice(fa):
