@@ -36,10 +36,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+_CSRC = "flashattention_kv_cache_amd/csrc/"
+_PREFILL_SRC = [_CSRC + "prefill_bf16.hip", _CSRC + "fa_internal.h"]
+_DECODE_SRC = [_CSRC + "decode.hip", _CSRC + "fa_internal.h", _CSRC + "fa_api.cpp"]  # fa_api.cpp: the split length
+# The files whose kernels (and launch choices) each traffic record in
+# profiles/traffic.json was measured on.
 KERNEL_SOURCES = {
-    "prefill": ["flashattention_kv_cache_amd/csrc/prefill_bf16.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
-    "decode": ["flashattention_kv_cache_amd/csrc/decode.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
-    "mla": ["flashattention_kv_cache_amd/csrc/mla_decode.hip", "flashattention_kv_cache_amd/csrc/fa_internal.h"],
+    "prefill": _PREFILL_SRC, "prefill_long": _PREFILL_SRC, "chunked_prefill": _PREFILL_SRC,
+    "window_prefill": _PREFILL_SRC,
+    "decode": _DECODE_SRC, "decode_contiguous": _DECODE_SRC, "fp8_decode": _DECODE_SRC, "window_decode": _DECODE_SRC,
+    "mla": [_CSRC + "mla_decode.hip", _CSRC + "fa_internal.h", _CSRC + "fa_api.cpp"],
+    "kv_append": [_CSRC + "kv_append.hip", _CSRC + "fa_internal.h"],
 }
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "prefill TFLOP/s & decode KV GB/s (% of MI355X peak), GQA d=128 bf16"
@@ -144,7 +151,8 @@ def extras(dev, steps: int, dec):
                            "kernel_ms_median": round(p_med, 5), "flops": w4.flops(),
                            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                        "kernel": "prefill_bf16_kernel<128, contiguous, no window>"}}
+                                        "kernel": "prefill_bf16_kernel<128, contiguous, no window>",
+                                        "traffic": measured_traffic("prefill_long")}}
     del q, k, v, o, lse
     w = W.CHUNKED
     ci = W.chunked_inputs(w)
@@ -179,14 +187,16 @@ def extras(dev, steps: int, dec):
                             "kernel_ms": round(c_avg, 5), "kernel_ms_median": round(c_med, 5), "flops": flops,
                             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                         "kernel": "prefill_bf16_kernel<128, paged, no window>"}},
+                                         "kernel": "prefill_bf16_kernel<128, paged, no window>",
+                                         "traffic": measured_traffic("chunked_prefill")}},
         "kv_append": {"workload": f"append of the same chunks ({w.B} x {w.chunk} tokens, {w.Hkv} KV heads, "
                                   f"d={w.d}, bf16) into the paged pool",
                       "value": round(gbs, 2), "unit": "GB/s", "kernel_ms": round(a_b2b, 5),
                       "kernel_ms_per_launch_events": round(a_avg, 5), "kernel_ms_median": round(a_med, 5),
                       "bytes": abytes,
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "kv_append_kernel"}},
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "kv_append_kernel",
+                                   "traffic": measured_traffic("kv_append")}},
     })
     del q, kn, vn, kc, vc, o, lse, ci
 
@@ -202,7 +212,8 @@ def extras(dev, steps: int, dec):
                              "kernel_ms": round(p_avg, 5), "kernel_ms_median": round(p_med, 5), "flops": wp.flops(),
                              "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                           "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                                          "kernel": "prefill_bf16_kernel<128, contiguous, window>"}}
+                                          "kernel": "prefill_bf16_kernel<128, contiguous, window>",
+                                          "traffic": measured_traffic("window_prefill")}}
     del q, k, v, o, lse
 
     # sliding window: decode over the resident batch
@@ -227,7 +238,8 @@ def extras(dev, steps: int, dec):
                             "kernel_ms_median": round(d_med, 5), "bytes": nbytes, "split_tokens": st,
                             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                         "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"}}
+                                         "kernel": "decode_split_kernel<bf16,128,4,paged> (one split per sequence)",
+                                         "traffic": measured_traffic("window_decode")}}
     out["window_decode"] = out_window
 
     # FP8 (E4M3) cache: the resident batch's cache rounded to E4M3 codes on the
@@ -255,7 +267,8 @@ def extras(dev, steps: int, dec):
                          "tokens_per_s": round(tokens / (f_avg * 1e-3), 1),
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                       "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                      "kernel": "decode_split_kernel<fp8,128,4,paged> + decode_merge_kernel"}}
+                                      "kernel": "decode_plan_kernel + decode_split_kernel<fp8,128,4,paged> + decode_merge_kernel",
+                                      "traffic": measured_traffic("fp8_decode")}}
     del fk, fv
 
     # decode against a contiguous cache (64 sequences, S_cap 8192)
@@ -276,7 +289,8 @@ def extras(dev, steps: int, dec):
                                 "split_tokens": st,
                                 "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                              "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                             "kernel": "decode_split_kernel<bf16,128,4,contiguous> + decode_merge_kernel"}}
+                                             "kernel": "decode_plan_kernel + decode_split_kernel<bf16,128,4,contiguous> + decode_merge_kernel",
+                                             "traffic": measured_traffic("decode_contiguous")}}
     del cq, ck, cv, co, di
 
     # MLA decode (absorbed latent form), DeepSeek-V3-shaped batch
@@ -312,7 +326,7 @@ def extras(dev, steps: int, dec):
                          # ridge point (2.5e15 / 8e12 = 312 flop/B): the floor is HBM time
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                       "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                      "kernel": "mla_split_kernel + mla_merge_kernel",
+                                      "kernel": "mla_plan_kernel + mla_split_kernel + mla_merge_kernel",
                                       "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                       "traffic": measured_traffic("mla")}}
     del mq, mkv, mo
@@ -488,7 +502,7 @@ def main():
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                             "algorithmic_bytes": dec_bytes,
-                            "kernel": "decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
+                            "kernel": "decode_plan_kernel + decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
         "wall_s_timed": round(wall, 4),
     }
     out["preconditioning"] = {"extras_first": extra is not None, "gpu_busy_s_before_warmup": round(busy_s, 2),
