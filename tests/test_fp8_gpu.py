@@ -111,6 +111,11 @@ DECODE_CASES = [
     (4, 8, 1, 128, [3, 64, 65, 1500], False, 0, 256, 0),
     (3, 16, 2, 64, [10, 300, 2500], True, 16, 256, 700),
     (2, 8, 8, 128, [4096, 5000], True, 32, 0, 0),
+    # a window over 4-token blocks, 1-token blocks with 16 query heads per KV head, and
+    # sequences shorter than one stage
+    (2, 16, 4, 128, [33, 2500], True, 4, 512, 300),
+    (3, 16, 1, 128, [1, 129, 1000], True, 1, 256, 0),
+    (3, 8, 2, 128, [31, 32, 5], False, 0, 256, 0),
 ]
 
 
