@@ -75,6 +75,9 @@ PREFILL_CASES = [
     (1, 4, 2, 700, 700, 128, True),       # three tiles: a pair plus the lone middle one
     (1, 2, 1, 1200, 1300, 64, True),      # five tiles, bottom-right mask, d = 64
     (2, 2, 2, 520, 520, 128, False),      # three tiles, no mask
+    # B * Hkv a multiple of 8: workgroups placed KV-head-major per XCD
+    (2, 16, 8, 700, 700, 128, True),      # two (sequence, KV head) groups per XCD, pairs + middle tile
+    (3, 8, 8, 300, 300, 64, True),        # three groups per XCD, MHA
 ]
 
 
