@@ -113,6 +113,28 @@ def test_prefill_scale_and_deterministic(fa):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_prepared_calls_match_direct_calls(fa):
+    """``prepare=True`` checks and marshals a call once; calling it again only
+    enqueues the kernels.  Three replays give the direct call's bits."""
+    q, k, v = W.make_prefill_inputs(1, 8, 2, 300, 300, 128, "bf16", seed=15)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_ref, l_ref = fa.prefill(qd, kd, vd, causal=True)
+    call, o, l = fa.prefill(qd, kd, vd, causal=True, prepare=True)
+    di = W.make_decode_inputs(3, 8, 2, 128, "bf16", seed=16, seq_lens=[900, 5, 2000], paged=True)
+    dargs = (di.q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.seq_lens.to(DEV))
+    dkw = dict(block_table=di.block_table.to(DEV), max_seq_len=di.max_seq_len, split_tokens=256)
+    do_ref, dl_ref = fa.decode(*dargs, **dkw)
+    dcall, do, dl = fa.decode(*dargs, prepare=True, **dkw)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        o.zero_(); l.zero_(); do.zero_(); dl.zero_()
+        call()
+        dcall()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+        assert torch.equal(do, do_ref) and torch.equal(dl, dl_ref)
+
+
 def test_prefill_writes_nothing_outside_its_output(fa):
     B, Hq, Hkv, N, d = 1, 4, 2, 100, 128
     q, k, v = W.make_prefill_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=6)
