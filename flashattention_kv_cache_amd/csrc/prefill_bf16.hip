@@ -53,6 +53,18 @@
 //     of the tiles and meets the barriers.
 //   * the output tile leaves through LDS (the K/V tiles are free by then), so
 //     that each global store writes 1 KiB of consecutive rows.
+//   * the weights of a tile are taken against the running max as it stands,
+//     without a pass over the tile's scores first: (m, l, O) is exact for
+//     any reference m, and what the reference must keep in check is the size
+//     of the weights.  A lane whose sum of the tile's weights exceeds
+//     2^kSlack (as any weight above 2^kSlack makes it) sends the wave back
+//     over the tile: S(t) again from K(t), read from global memory since its
+//     LDS buffer is being refilled, then its exact max, the rescale and new
+//     weights.  Only a wave's first tile takes its max first.  This removes
+//     the max's ~30 vector instructions per stage, which at the clock the
+//     matrix cores' power allows cost time as vector work.  With a sliding
+//     window, whose rows find their first keys tiles apart, the max still
+//     comes first.
 //   * the row sum is accumulated in fp32 from the unrounded weights (a sum of
 //     the bf16-rounded weights would move the log-sum-exp by ~1e-3 on short
 //     rows).
@@ -69,6 +81,7 @@ constexpr int kBN = 64;   // keys per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCopyRows = kBN / kWaves;  // tile rows one wave copies
 constexpr float kSlack = 8.f;  // log2 units a running max may lag before rescaling
+constexpr float kSumMax = 256.f;  // 2^kSlack: largest accepted sum of a lane's weights of one tile
 
 template <int D>
 struct Smem {
@@ -378,7 +391,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     for (int i = 0; i < DB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-    float m = -INFINITY, l0 = 0.f, l1 = 0.f;
+    // m: running max (log2 units, -inf before a row's first key); mref: the
+    // reference the weights are taken against (m, or 0 while m is -inf)
+    float m = -INFINITY, mref = 0.f, l0 = 0.f, l1 = 0.f;
     const float c = a.scale * kLog2e;
 
     using KCopy = typename std::conditional<PAGED, PagedCopy<D, false>, TileCopy<D, false>>::type;
@@ -509,8 +524,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     };
     // Running max of tile t; a rescale it calls for applies to l now and to O
     // at the start of the next stage, after PV(t-1).  Returns the reference
-    // the weights of tile t are taken against.
-    auto softmax_ref = [&](f32x16_t (&sc)[2], int t) {
+    // the weights of tile t are taken against (also kept in mref).
+    auto softmax_ref = [&](f32x16_t (&sc)[2], int t, float slack) {
       if (t >= n_clean || t < n_lo) mask(sc, t);
       float mx = sc[0][0];
 #pragma unroll
@@ -518,18 +533,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = max_nan(mx, sc[1][r]);
       mx = halves_max_nan(mx) * c;
-      // Rescale only when some row's max grows by more than kSlack (log2
-      // units): (m, l, O) stays exact for any reference m within kSlack of the
-      // true max, and P is then at most 2^kSlack (fine in bf16).
+      // Rescale only when some row's max grows by more than `slack` (log2
+      // units): (m, l, O) stays exact for any reference m within the slack
+      // of the true max, and P is then at most 2^slack (fine in bf16).
       const float mn = max_nan(m, mx);
-      if (__any(mn > m + kSlack)) {
+      if (__any(mn > m + slack)) {
         pend_alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
         pending = true;
         l0 *= pend_alpha;
         l1 *= pend_alpha;
         m = mn;
       }
-      return (m == -INFINITY) ? 0.f : m;
+      mref = (m == -INFINITY) ? 0.f : m;
+      return mref;
+    };
+    // S(t) again, from K in global memory: the same MFMAs on the same operands
+    // as qk() on the LDS tile, so the same scores (rows outside [kbeg, Nk) are
+    // read clamped, as the tile copies do, and masked afterwards).
+    auto qk_global = [&](f32x16_t (&sacc)[2], int t) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int tok = min(max(t * kBN + kb * 32 + col, kbeg), Nk - 1);
+        const uint16_t* kr;
+        if constexpr (PAGED)
+          kr = kg + ((size_t)trow[tok >> lbs] * bsz + (tok & (bsz - 1))) * slot_elems;
+        else
+          kr = kg + (size_t)tok * D;
+        bf16x8_t kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 16 + hl * 8);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], ks == 0 ? f32x16_t{} : sacc[kb], 0, 0, 0);
+        asm volatile("" ::: "memory");  // one key block's operands in registers at a time
+      }
     };
     auto stage_end = [&]() {
       wait_all_vmem();  // this wave's direct loads have landed
@@ -556,12 +593,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       bf16x8_t ka_n = k_operand(0), va_n{};
       if (with_pv) va_n = v_operand(0);
 
-      const float mu = softmax_ref(sc, t);
+      // The weights of tile t are taken against the reference as it stands;
+      // the tile's own max is looked at only if they come out too large
+      // (below).  With a sliding window, whose rows find their first keys
+      // tiles apart, the max comes first as before.
+      float mu;
+      if constexpr (WINDOW) {
+        mu = softmax_ref(sc, t, kSlack);
+      } else {
+        if (t >= n_clean || t < n_lo) mask(sc, t);
+        mu = mref;
+      }
 
       // ---- matrix cores: S(t+1) and O += V(t-1) P(t-1); vector ALUs: P(t),
       // packed to bf16 pairs as they are made.  PV(t-1) has 4 * DB = 2 * KS
       // MFMAs, as many as QK^T: one per k-step.
       u32x4_t w[4];
+      float ps0 = 0.f, ps1 = 0.f;  // this lane's sums of the tile's weights
 #pragma unroll
       for (int j = 0; j < 2 * KS; ++j) {
         const int kb = j / KS, ks = j % KS;
@@ -577,8 +625,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
           const int r = ks * VPS + i;  // register r of block kb: element r % 8 of half r / 8
           const float p0 = fast_exp2(fmaf(sc[kb][r], c, -mu));
           const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c, -mu));
-          l0 += p0;
-          l1 += p1;
+          if constexpr (WINDOW) {
+            l0 += p0;
+            l1 += p1;
+          } else {
+            ps0 += p0;
+            ps1 += p1;
+          }
           w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
         }
         // interleave: each MFMA, then some of the next group's LDS reads (K
@@ -590,6 +643,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      }
+      // A lane's sum above 2^kSlack (as any weight above 2^kSlack makes it),
+      // or a row still without a reference: the tile again, against its
+      // exact max.  NaN sums (NaN scores) pass, as NaN maxima do.
+      if (!WINDOW && __any(ps0 + ps1 > kSumMax || m == -INFINITY)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin(w[i]);  // the first weights are made among the MFMAs all the same
+        qk_global(sc, t);
+        const float mu2 = softmax_ref(sc, t, 0.f);
+        ps0 = ps1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(sc[kb][r], c, -mu2));
+            const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c, -mu2));
+            ps0 += p0;
+            ps1 += p1;
+            w[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+          }
+      }
+      if constexpr (!WINDOW) {
+        l0 += ps0;
+        l1 += ps1;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -611,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
                           auto with_pv) {
       stage_start(t);
       if constexpr (decltype(softmax)::value) {
-        const float mu = softmax_ref(sc, t);
+        const float mu = softmax_ref(sc, t, kSlack);
         u32x4_t w[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -680,6 +757,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         qk(s_a, tl & 1);
         stage_end();
       }
+      // the wave's first tile: its exact max first, so that its weights pass
+      // the check
+      if constexpr (!WINDOW) softmax_ref(s_a, tl, 0.f);
       stage(s_a, s_b, p_b, p_a, tl, false);
       int t = tl + 1;
       // full stages while S(t+1) still has a key this wave sees
