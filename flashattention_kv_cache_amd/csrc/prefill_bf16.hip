@@ -315,6 +315,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     b = bh / a.Hq;
     h = bh % a.Hq;
   }
+  // The work item is the same for every lane.  In the longest-first path it
+  // comes out of LDS, which the compiler treats as per-lane, so it is made
+  // scalar explicitly: the K/V head addresses built from it must sit in
+  // scalar registers, where the direct-load assembly takes its base.
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  pr = __builtin_amdgcn_readfirstlane(pr);
+  single = __builtin_amdgcn_readfirstlane(single);
   const int g = h / n_rep;
 
   const int lane = threadIdx.x & 63;
