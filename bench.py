@@ -65,6 +65,9 @@ def parse():
                    help="after timing, run one device copy of this many MiB (a known-size kernel for HBM counters)")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the measurements outside the step (KV append, chunked prefill)")
+    p.add_argument("--power-seconds", type=float, default=0.0,
+                   help="after timing, run the prefill and then the decode alone for this many seconds each "
+                        "while sampling board power and shader clocks with amd-smi (0 = off)")
     return p.parse_args()
 
 
@@ -333,6 +336,76 @@ def extras(dev, steps: int, dec):
     return out
 
 
+def parse_smi_metric(text: str):
+    """(socket power in W, [shader clock of each XCD in MHz]) from the text of
+    ``amd-smi metric -p -c``; None where the field is absent."""
+    watts, gfx, block = None, [], None
+    for line in text.splitlines():
+        t = line.strip()
+        if t.startswith("SOCKET_POWER:"):
+            try:
+                watts = float(t.split(":")[1].split()[0])
+            except ValueError:
+                watts = None
+        elif t.endswith(":") and " " not in t:
+            block = t[:-1]
+        elif t.startswith("CLK:") and block is not None and block.startswith("GFX_"):
+            try:
+                gfx.append(float(t.split(":")[1].split()[0]))
+            except ValueError:
+                pass
+    return watts, gfx
+
+
+def power_clock(torch, calls, seconds: float):
+    """Board power and shader clocks while each call runs back to back for
+    `seconds`: the power the board draws under that kernel and the clock it
+    holds there.  amd-smi refreshes its readings about every 0.75 s, so the
+    first second of each run is skipped and the rest sampled every 0.25 s."""
+    import shutil
+    import subprocess
+    import threading
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(smi):
+        return {"error": "amd-smi not found"}
+    res = {}
+    for name, call, batch in calls:
+        samples = []
+        stop = threading.Event()
+
+        def sample():
+            time.sleep(1.0)
+            while not stop.is_set():
+                r = subprocess.run([smi, "metric", "-p", "-c", "-g", "0"], capture_output=True, text=True)
+                samples.append(parse_smi_metric(r.stdout))
+                time.sleep(0.25)
+
+        th = threading.Thread(target=sample)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 0
+        t_end = time.perf_counter() + seconds
+        e0.record()
+        th.start()
+        while time.perf_counter() < t_end:
+            for _ in range(batch):
+                call()
+            n += batch
+            torch.cuda.synchronize()
+        e1.record()
+        stop.set()
+        th.join()
+        torch.cuda.synchronize()
+        watts = [w for w, _ in samples if w is not None]
+        clocks = [sum(g) / len(g) for _, g in samples if g]
+        res[name] = {"launches": n, "kernel_us": round(e0.elapsed_time(e1) / n * 1000, 2), "samples": len(samples),
+                     "socket_w_mean": round(sum(watts) / len(watts), 1) if watts else None,
+                     "socket_w_max": max(watts) if watts else None,
+                     "gfx_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
+                     "gfx_mhz_min_xcd": min(min(g) for _, g in samples if g) if clocks else None,
+                     "gfx_mhz_max_xcd": max(max(g) for _, g in samples if g) if clocks else None}
+    return res
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workloads:
     whole (b, h) heads of the prefill until about budget_s seconds have passed,
@@ -510,6 +583,9 @@ def main():
                             "kernel": "decode_plan_kernel + decode_split_kernel<bf16,128,4,paged> + decode_merge_kernel"},
         "wall_s_timed": round(wall, 4),
     }
+    if args.power_seconds > 0:
+        out["power_clock"] = power_clock(torch, [("prefill", prefill, 2000), ("decode", decode, 200)],
+                                         args.power_seconds)
     out["preconditioning"] = {"extras_first": extra is not None, "gpu_busy_s_before_warmup": round(busy_s, 2),
                               "warmup_steps": args.warmup}
     if extra is not None:

@@ -45,3 +45,30 @@ def test_traffic_within_a_few_percent_of_the_algorithmic_bytes_for_the_step():
         pytest.skip("kernel sources changed since the counters were taken")
     assert 8_641_433_236 <= dec <= 1.01 * 8_641_433_236
     assert 84_410_368 <= pre <= 1.05 * 84_410_368
+
+
+_SMI_SAMPLE = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1286 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1764 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1727 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 2000 MHz
+        VCLK_0:
+            CLK: 59 MHz
+"""
+
+
+def test_power_and_shader_clocks_are_read_from_amd_smi_text():
+    watts, gfx = bench.parse_smi_metric(_SMI_SAMPLE)
+    assert watts == 1286.0
+    assert gfx == [1764.0, 1727.0]  # memory and video clocks are not shader clocks
+    assert bench.parse_smi_metric("SOCKET_POWER: N/A\n") == (None, [])
