@@ -12,7 +12,13 @@
 //
 // gfx950 mapping (not from the pages):
 //   * workgroup = 8 waves = 256 query rows, one workgroup per CU (two waves
-//     per SIMD); each wave owns 32 rows.  Both waves of a SIMD belong to the
+//     per SIMD); each wave owns 32 rows.  The rows are 256 / hw consecutive
+//     positions of hw query heads that read the same KV head (hw = the
+//     largest power of two dividing Hq / Hkv, at most 8): every K/V tile
+//     still feeds 256 rows, while a query tile spans fewer positions, so the
+//     causal diagonal crosses fewer key tiles (one instead of four at
+//     Hq / Hkv = 4; measured on MI355X at N = 4096: 2.8% less time than 256
+//     positions of one head, same bits).  Both waves of a SIMD belong to the
 //     same workgroup, so neither can starve the other (two co-resident
 //     workgroups were measured to progress at rates ~1.4x apart, leaving each
 //     CU's last stretch to a single workgroup).  Key and
@@ -198,12 +204,21 @@ struct PagedCopy {
   }
 };
 
-// Key tiles that query tile qb of sequence b visits (the key range run_tile
-// computes): with a cache (seq_lens) the sequences differ in length.
-__device__ __forceinline__ int tile_count(const PrefillArgs& a, int W, int b, int qb) {
+// Query heads that share a workgroup: the largest power of two dividing
+// n_rep = Hq / Hkv, at most 8.  All of them read the same KV head, and the
+// workgroup's 256 rows are 256 / hw consecutive positions of each.
+__host__ __device__ __forceinline__ int heads_per_workgroup(int n_rep) {
+  const int p = n_rep & -n_rep;
+  return p < 8 ? p : 8;
+}
+
+// Key tiles that query tile qb (P positions) of sequence b visits (the key
+// range run_tile computes): with a cache (seq_lens) the sequences differ in
+// length.
+__device__ __forceinline__ int tile_count(const PrefillArgs& a, int W, int P, int b, int qb) {
   const int L = a.seq_lens[b];
   if (L < 0 || L > a.max_seq_len || (a.causal && L < a.Nq)) return 0;
-  const int off = L - a.Nq, q0 = qb * kBM, last = min(a.Nq, q0 + kBM) - 1;
+  const int off = L - a.Nq, q0 = qb * P, last = min(a.Nq, q0 + P) - 1;
   const int kend = a.causal ? min(L, last + off + 1) : L;
   const int tb = (W > 0 ? max(0, q0 + off - W + 1) : 0) / kBN;
   return max(tb, (kend + kBN - 1) / kBN) - tb;
@@ -217,12 +232,12 @@ __device__ __forceinline__ int tile_count(const PrefillArgs& a, int W, int b, in
 // the workgroups of a launch take every item exactly once.  `scratch` holds
 // kLptBuckets + 8 words of LDS; all threads of the workgroup call this.
 constexpr int kLptBuckets = 1024;  // counts past the last bucket share it (ordered by index)
-__device__ int lpt_item(const PrefillArgs& a, int W, int nqb, int r, uint32_t* scratch) {
+__device__ int lpt_item(const PrefillArgs& a, int W, int P, int nqb, int r, uint32_t* scratch) {
   uint32_t* hist = scratch;                  // bucket 0 = the most key tiles
   uint32_t* wsum = scratch + kLptBuckets;    // per-wave totals of a scan (8)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = a.B * nqb;
-  auto bucket = [&](int i) { return kLptBuckets - 1 - min(tile_count(a, W, i / nqb, i % nqb), kLptBuckets - 1); };
+  auto bucket = [&](int i) { return kLptBuckets - 1 - min(tile_count(a, W, P, i / nqb, i % nqb), kLptBuckets - 1); };
   for (int i = tid; i < kLptBuckets; i += kThreads) hist[i] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += kThreads) atomicAdd(&hist[bucket(i)], 1u);
@@ -280,40 +295,48 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int VPS = 16 / KS; // softmax values of one 32-key block per QK^T k-step
 
-  // ---- work item.  Sequences of one length (plain prefill, or a single
-  // cached sequence): (b, h, pair of query tiles), KV-head-major per XCD.  A
+  // ---- work item: a sequence b, hw query heads h .. h + hw - 1 of one KV
+  // head, and query tiles of P = 256 / hw positions.  Sequences of one
+  // length (plain prefill, or a single cached sequence): (b, h, pair of query
+  // tiles), KV-head-major per XCD.  A
   // workgroup takes query tiles nqb - 1 - pr and pr of one head: with a
   // causal mask their key-tile counts add up to the same total for every
   // pair, so all workgroups carry equal work (the lone middle tile of an odd
   // count comes last).  Cached sequences of different lengths (lpt): one
   // query tile per workgroup, the (sequence, tile) items taken longest first
   // so that the hardware's in-order dispatch onto free CUs balances them; the
-  // Hq workgroups of an item are consecutive, each XCD getting whole KV-head
-  // groups.
+  // Hq / hw workgroups of an item are consecutive, each XCD getting whole
+  // KV-head groups.
   const int id = blockIdx.x;
   const int n_rep = a.Hq / a.Hkv;
+  const int hw = heads_per_workgroup(n_rep);  // query heads per workgroup
+  const int lhw = __builtin_ctz(hw);
+  const int nw = n_rep >> lhw;                // workgroups per (sequence, KV head, query tile)
+  const int P = kBM >> lhw;                   // query positions per tile
   const int GP = a.B * a.Hkv;
-  int b, h, pr, single = -1;
+  int b, h, pr, single = -1;                  // h: the workgroup's first query head
   if (lpt) {
-    const int item = lpt_item(a, WINDOW ? a.window : 0, nqb, id / a.Hq, reinterpret_cast<uint32_t*>(sm.k[0]));
-    const int j = id % a.Hq;
+    const int per_item = a.Hkv * nw;
+    const int item = lpt_item(a, WINDOW ? a.window : 0, P, nqb, id / per_item, reinterpret_cast<uint32_t*>(sm.k[0]));
+    const int j = id % per_item;
     b = item / nqb;
     single = item % nqb;
     pr = 0;
-    h = (j % a.Hkv) * n_rep + j / a.Hkv;
+    h = (j % a.Hkv) * n_rep + (j / a.Hkv) * hw;
   } else if ((GP & 7) == 0) {
     const int xcd = id & 7, j = id >> 3;
-    const int per = (GP >> 3) * n_rep;  // work items per pair rank on one XCD
+    const int per = (GP >> 3) * nw;  // work items per pair rank on one XCD
     const int rest = j % per;
     pr = j / per;
-    const int gp = xcd + 8 * (rest / n_rep);
+    const int gp = xcd + 8 * (rest / nw);
     b = gp / a.Hkv;
-    h = (gp % a.Hkv) * n_rep + rest % n_rep;
+    h = (gp % a.Hkv) * n_rep + (rest % nw) * hw;
   } else {
-    const int bh = id % (a.B * a.Hq);
-    pr = id / (a.B * a.Hq);
-    b = bh / a.Hq;
-    h = bh % a.Hq;
+    const int units = GP * nw;  // workgroups per pair rank
+    const int bh = id % units;
+    pr = id / units;
+    b = bh / (a.Hkv * nw);
+    h = (bh % (a.Hkv * nw)) * hw;  // (KV head g, sub-group s) -> first head g * n_rep + s * hw
   }
   // The work item is the same for every lane.  In the longest-first path it
   // comes out of LDS, which the compiler treats as per-lane, so it is made
@@ -329,6 +352,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;   // which half of the wave
   const int col = lane & 31;  // query column within the wave's 32 rows
+  // wave w: query head h + w % hw, positions 32 * (w / hw) .. + 31 of the tile
+  const int hq = h + (wave & (hw - 1));
+  const int pw = (wave >> lhw) * 32;
 
   // ---- the keys: Nk of them per head, or the cached length of sequence b
   // (the queries being its newest tokens).  A length outside the contract, or
@@ -350,9 +376,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 
   // One query tile: everything from the key range to the epilogue.
   auto run_tile = [&](const int qb) {
-    const int q0 = qb * kBM;
+    const int q0 = qb * P;
     bool bad = bad_seq;
-    const int last_row = min(a.Nq, q0 + kBM) - 1;
+    const int last_row = min(a.Nq, q0 + P) - 1;
     int kend = a.causal ? min(Nk, last_row + off + 1) : Nk;
     // first key any row of the workgroup sees (its first row's window start)
     const int kbeg = W > 0 ? max(0, q0 + off - W + 1) : 0;
@@ -378,18 +404,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     const int n_clean = a.causal ? min((q0 + off + 1) / kBN, Nk / kBN) : Nk / kBN;
     const int n_lo = W > 0 ? (max(0, last_row + off - W + 1) + kBN - 1) / kBN : 0;
     // causal: tiles [tb, te_w) hold a key that some row of this wave sees
-    const int te_w = a.causal ? min(te, max(tb, (min(q0 + wave * 32 + 31, a.Nq - 1) + off) / kBN + 1)) : te;
+    const int te_w = a.causal ? min(te, max(tb, (min(q0 + pw + 31, a.Nq - 1) + off) / kBN + 1)) : te;
     // window: this wave's rows see no key before tile tl_w; when tl > tb the
     // wave skips the products of tiles tb .. tl - 1 (exact zeros) and starts
     // its pipeline at tl
-    const int tl_w = W > 0 ? max(0, q0 + wave * 32 + off - W + 1) / kBN : tb;
+    const int tl_w = W > 0 ? max(0, q0 + pw + off - W + 1) / kBN : tb;
     const int tl = (tl_w > tb && tl_w < te_w) ? tl_w : tb;
 
     // ---- Q^T operand fragments, kept in registers
-    const int qrow = q0 + wave * 32 + col;
+    const int qrow = q0 + pw + col;
     bf16x8_t qf[KS];
     {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq + min(qrow, a.Nq - 1)) * D;
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(b * a.Hq + hq) * a.Nq + min(qrow, a.Nq - 1)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16 + hl * 8);
     }
@@ -828,15 +854,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // shorter launches at N = 4096, where the last tile's output is written
     // right before the kernel ends).
     constexpr int CPR = D / 8;  // 16-byte chunks per row
-    uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + q0 + wave * 32) * D;
+    uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Nq + q0 + pw) * D;
 #pragma unroll
     for (int i = 0; i < 32 * CPR / 64; ++i) {
       const int u = i * 64 + elane, r = u / CPR, ch = u % CPR;
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + r * D + ((ch ^ k_swz<D>(r)) * 8));
-      if (q0 + wave * 32 + r < a.Nq) __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(obase + r * D + ch * 8));
+      if (q0 + pw + r < a.Nq) __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(obase + r * D + ch * 8));
     }
     if (a.lse && hl == 0 && qrow < a.Nq)
-      a.lse[(size_t)(b * a.Hq + h) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+      a.lse[(size_t)(b * a.Hq + hq) * a.Nq + qrow] = bad ? __builtin_nanf("") : lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
   };
   if (single >= 0) {
     run_tile(single);
@@ -852,11 +878,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  const int nqb = (a.Nq + kBM - 1) / kBM;
+  const int hw = heads_per_workgroup(a.Hq / a.Hkv);
+  const int P = kBM / hw;  // query positions per tile
+  const int nqb = (a.Nq + P - 1) / P;
   // several cached sequences (lengths known only to the device): single query
   // tiles, longest first; otherwise pairs of query tiles
   const int lpt = a.seq_lens != nullptr && a.B > 1;
-  const long long grid = (long long)(lpt ? nqb : (nqb + 1) / 2) * a.Hq * a.B;
+  const long long grid = (long long)(lpt ? nqb : (nqb + 1) / 2) * (a.Hq / hw) * a.B;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool paged = a.block_table != nullptr, win = a.window > 0;
 #define FA_LAUNCH(DD, PG, WN) \

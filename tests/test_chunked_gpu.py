@@ -123,6 +123,10 @@ CHUNK_CASES = [
     (2, 4, 2, 128, 40, [100, 10], True, 16, False, 0),     # every query sees the whole cache
     (2, 4, 2, 128, 600, [100, 1000], True, 8, True, 0),    # three 256-row query tiles; blocks of a wave's 8 rows
     (1, 4, 2, 64, 530, [70], True, 16, True, 0),           # three query tiles, d = 64
+    # several query heads per workgroup (the largest power of two dividing Hq / Hkv, at most 8)
+    (3, 16, 1, 128, 90, [40, 300, 0], True, 16, True, 0),  # 8 heads x 32 positions, two workgroups per tile
+    (2, 12, 2, 128, 150, [77, 500], True, 8, True, 0),     # 2 heads x 128 positions, three workgroups per tile
+    (2, 8, 2, 64, 200, [10, 333], False, 0, True, 0),      # 4 heads x 64 positions, contiguous cache
 ]
 
 
@@ -153,8 +157,9 @@ def test_chunked_prefill_small(fa, case, dt):
 @pytest.mark.parametrize("paged", [True, False], ids=["paged", "contig"])
 def test_chunked_prefill_many_sequences_longest_first(fa, paged):
     """Several cached sequences run one query tile per workgroup, taken
-    longest first from a work list every workgroup computes alike.  640
-    (sequence, tile) items (more than one 512-item pass of the selection),
+    longest first from a work list every workgroup computes alike.  1280
+    (sequence, tile) items of 128 positions of both query heads (more than
+    one 512-item pass of the selection),
     lengths with many ties, and two sequences that break the contract (their
     rows must come out NaN): every item is computed exactly once."""
     B, Hq, Hkv, d, n = 160, 2, 1, 64, 1000

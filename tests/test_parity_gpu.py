@@ -78,6 +78,14 @@ PREFILL_CASES = [
     # B * Hkv a multiple of 8: workgroups placed KV-head-major per XCD
     (2, 16, 8, 700, 700, 128, True),      # two (sequence, KV head) groups per XCD, pairs + middle tile
     (3, 8, 8, 300, 300, 64, True),        # three groups per XCD, MHA
+    # query heads of one KV head share a workgroup (hw = the largest power of
+    # two dividing Hq / Hkv, at most 8): 256 / hw positions of hw heads each
+    (1, 16, 1, 300, 300, 128, True),      # Hq/Hkv 16: 8 heads x 32 positions, two workgroups per tile
+    (1, 12, 2, 333, 333, 128, True),      # Hq/Hkv 6: 2 heads x 128 positions, three workgroups per tile
+    (2, 24, 2, 250, 260, 64, True),       # Hq/Hkv 12: 4 heads x 64 positions, bottom-right mask
+    (1, 32, 8, 520, 520, 128, True),      # Hq/Hkv 4, B * Hkv = 8: per-XCD placement of 64-position tiles
+    (2, 64, 4, 200, 200, 128, True),      # Hq/Hkv 16, B * Hkv = 8: per-XCD placement, two workgroups per group
+    (1, 16, 2, 100, 130, 128, False),     # Hq/Hkv 8, no mask
 ]
 
 
