@@ -20,6 +20,10 @@ warm-up, see ``preconditioning``) times the KV append,
 the chunked prefill against a paged cache, sliding-window prefill and decode,
 decode against an FP8 cache, the long-context prefill (N = 32768) and decode
 against a contiguous cache, and MLA decode, each on its own.
+``--power-seconds S`` (outside the step, after the timing) runs the step's
+prefill and then its decode back to back for S seconds each and reports the
+board power and the per-XCD shader clocks amd-smi reads meanwhile
+(``power_clock``).
 """
 from __future__ import annotations
 
