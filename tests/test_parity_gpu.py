@@ -283,7 +283,8 @@ def _sample_rows(w, rng, n_random):
 def one_head_per_kv_head(w):
     """A query head of every KV head, each at a different position within its
     group: every KV head (and with it every XCD slot of the launch's
-    KV-head-major mapping) and every query-tile pair is covered."""
+    KV-head-major mapping), every query-tile pair, and every place a head
+    takes among the query heads that share a workgroup is covered."""
     n_rep = w.Hq // w.Hkv
     return [(b, g * n_rep + (g + b) % n_rep) for b in range(w.B) for g in range(w.Hkv)]
 
@@ -321,8 +322,9 @@ def c4_run(fa):
 
 
 def test_workload_prefill_full_size_C4_whole_heads(c4_run):
-    """N = 32768: every row of one query head per KV head (all 64 query-tile
-    pairs of the launch, every KV head) against the oracle."""
+    """N = 32768: every row of one query head per KV head (all 512 query-tile
+    pairs of the launch, every KV head, each of the 8 places of a head in its
+    workgroup) against the oracle."""
     w, q, k, v, o_c, lse_c = c4_run
     assert torch.isfinite(o_c.float()).all() and torch.isfinite(lse_c).all()
     heads = one_head_per_kv_head(w)
