@@ -86,6 +86,7 @@ PREFILL_CASES = [
     (1, 32, 8, 520, 520, 128, True),      # Hq/Hkv 4, B * Hkv = 8: per-XCD placement of 64-position tiles
     (2, 64, 4, 200, 200, 128, True),      # Hq/Hkv 16, B * Hkv = 8: per-XCD placement, two workgroups per group
     (1, 16, 2, 100, 130, 128, False),     # Hq/Hkv 8, no mask
+    (1, 32, 1, 290, 290, 128, True),      # MQA with 32 heads: 8 heads x 32 positions, four workgroups per tile
 ]
 
 
