@@ -121,8 +121,8 @@ CHUNK_CASES = [
     (2, 4, 2, 128, 70, [130, 0], False, 0, True, 0),       # contiguous cache
     (2, 8, 4, 64, 100, [20, 300], False, 0, True, 0),
     (2, 4, 2, 128, 40, [100, 10], True, 16, False, 0),     # every query sees the whole cache
-    (2, 4, 2, 128, 600, [100, 1000], True, 8, True, 0),    # three 256-row query tiles; blocks of a wave's 8 rows
-    (1, 4, 2, 64, 530, [70], True, 16, True, 0),           # three query tiles, d = 64
+    (2, 4, 2, 128, 600, [100, 1000], True, 8, True, 0),    # five 128-position query tiles; blocks of a wave's 8 rows
+    (1, 4, 2, 64, 530, [70], True, 16, True, 0),           # five 128-position query tiles, d = 64
     # several query heads per workgroup (the largest power of two dividing Hq / Hkv, at most 8)
     (3, 16, 1, 128, 90, [40, 300, 0], True, 16, True, 0),  # 8 heads x 32 positions, two workgroups per tile
     (2, 12, 2, 128, 150, [77, 500], True, 8, True, 0),     # 2 heads x 128 positions, three workgroups per tile

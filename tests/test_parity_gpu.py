@@ -70,11 +70,13 @@ PREFILL_CASES = [
     (2, 2, 1, 127, 300, 128, False),      # Nq != Nk
     (1, 4, 2, 70, 200, 128, True),        # chunked prefill, bottom-right mask
     (1, 4, 2, 1, 333, 64, True),          # a single new query against a cache
-    (1, 2, 2, 383, 383, 128, True),       # three query tiles, ragged
-    # the bf16 kernel runs query tiles of 256 rows in complementary pairs:
-    (1, 4, 2, 700, 700, 128, True),       # three tiles: a pair plus the lone middle one
-    (1, 2, 1, 1200, 1300, 64, True),      # five tiles, bottom-right mask, d = 64
-    (2, 2, 2, 520, 520, 128, False),      # three tiles, no mask
+    (1, 2, 2, 383, 383, 128, True),       # two 256-position tiles (MHA), ragged
+    # the bf16 kernel runs query tiles (256 rows: 256 / hw positions of hw
+    # heads) in complementary pairs; an odd count leaves a lone middle tile:
+    (1, 4, 2, 700, 700, 128, True),       # six 128-position tiles: three pairs
+    (1, 2, 1, 1200, 1300, 64, True),      # ten 128-position tiles, bottom-right mask, d = 64
+    (2, 2, 2, 520, 520, 128, False),      # three 256-position tiles: a pair plus the lone middle one, no mask
+    (1, 4, 1, 300, 300, 128, True),       # five 64-position tiles: two pairs plus the lone middle one
     # B * Hkv a multiple of 8: workgroups placed KV-head-major per XCD
     (2, 16, 8, 700, 700, 128, True),      # two (sequence, KV head) groups per XCD, pairs + middle tile
     (3, 8, 8, 300, 300, 64, True),        # three groups per XCD, MHA

@@ -67,7 +67,8 @@ PREFILL_CASES = [
     (1, 4, 1, 257, 257, 64, 129),
     (1, 4, 2, 70, 333, 128, 90),       # queries extend a cache: bottom-right
     (2, 2, 2, 520, 520, 64, 256),
-    (1, 4, 2, 1100, 1100, 128, 300),   # five 256-row query tiles in pairs
+    (1, 4, 2, 1100, 1100, 128, 300),   # nine 128-position query tiles (2 heads each) in pairs
+    (1, 8, 2, 700, 700, 128, 200),     # eleven 64-position tiles (4 heads each); waves start their windows tiles apart
 ]
 
 
