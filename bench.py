@@ -588,8 +588,23 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if args.power_seconds > 0:
-        out["power_clock"] = power_clock(torch, [("prefill", prefill, 2000), ("decode", decode, 200)],
-                                         args.power_seconds)
+        # the step's two kernels, then the prefill's per-workgroup work on half
+        # and a quarter of the CUs (C2's sequence length and head layout per
+        # KV head, fewer KV heads): does the clock, and with it the
+        # per-workgroup time, rise when fewer CUs draw power?
+        calls = [("prefill", prefill, 2000), ("decode", decode, 200)]
+        keep = []
+        for hq, hkv in ((16, 4), (8, 2)):
+            pq, pk, pv = (t.to(dev) for t in W.make_prefill_inputs(1, hq, hkv, wp.Nq, wp.Nk, wp.d, "bf16", wp.seed))
+            c = binding.prefill(pq, pk, pv, causal=True, scale=wp.scale, prepare=True)[0]
+            keep.append((pq, pk, pv))
+            calls.append((f"prefill_Hq{hq}_Hkv{hkv}", c, 2000))
+        out["power_clock"] = power_clock(torch, calls, args.power_seconds)
+        # Hq / Hkv = 4: a workgroup holds 64 positions of 4 heads, two tiles
+        for name, hkv in (("prefill", wp.Hkv), ("prefill_Hq16_Hkv4", 4), ("prefill_Hq8_Hkv2", 2)):
+            if name in out["power_clock"]:
+                out["power_clock"][name]["workgroups"] = hkv * wp.Nq // 64 // 2
+        del keep
     out["preconditioning"] = {"extras_first": extra is not None, "gpu_busy_s_before_warmup": round(busy_s, 2),
                               "warmup_steps": args.warmup}
     if extra is not None:
