@@ -57,11 +57,19 @@ def _heads(r):
     return hkv * rep, hkv
 
 
-def _prefill_cases(n, seed):
+def _group_heads(r):
+    # query heads per KV head whose largest power-of-two divisor is 2, 4 or 8:
+    # 2, 4 or 8 heads share a prefill workgroup, in 3 or more workgroups per tile
+    hkv = r.choice([1, 2])
+    return hkv * r.choice([6, 12, 16, 24, 32]), hkv
+
+
+def _prefill_cases(n, seed, heads=None):
+    heads = heads or _heads
     r = random.Random(seed)
     cases = []
     for _ in range(n):
-        hq, hkv = _heads(r)
+        hq, hkv = heads(r)
         d = r.choice([64, 128])
         dt = "f32" if r.random() < 0.2 else "bf16"
         causal = r.random() < 0.7
@@ -89,11 +97,12 @@ def _decode_cases(n, seed):
     return cases
 
 
-def _chunk_cases(n, seed):
+def _chunk_cases(n, seed, heads=None):
+    heads = heads or _heads
     r = random.Random(seed)
     cases = []
     for _ in range(n):
-        hq, hkv = _heads(r)
+        hq, hkv = heads(r)
         d = r.choice([64, 128])
         dt = "f32" if r.random() < 0.2 else "bf16"
         B = r.randint(1, 3)
@@ -121,9 +130,9 @@ def _mla_cases(n, seed):
     return cases
 
 
-PREFILL = _prefill_cases(24, 20261)
+PREFILL = _prefill_cases(24, 20261) + _prefill_cases(10, 20265, _group_heads)
 DECODE = _decode_cases(24, 20262)
-CHUNKED = _chunk_cases(16, 20263)
+CHUNKED = _chunk_cases(16, 20263) + _chunk_cases(6, 20266, _group_heads)
 FP8 = [c for c in _decode_cases(12, 20264)]
 MLA = _mla_cases(16, 20265)
 
